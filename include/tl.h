@@ -1,0 +1,174 @@
+/*
+ * tl.h -- C ABI of the paged KV-cache write and paged attention library (libtl.so),
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the two serving-graph ops of the page "How serving works in
+ * Tlaloc" (section 1, the decoder graph; section 2, their lowering):
+ *   KV_CACHE_WRITE   store each new token's key and value rows into a page pool at
+ *                    the token's slot; slot -1 is never written;
+ *   PAGED_ATTENTION  attend over the pages a per-sequence block table names, for a
+ *                    decode entry (one new token per sequence) or a prefill entry
+ *                    (right-aligned rows, causal length = position + 1), optionally
+ *                    with a sliding window (section 3, "Sliding-window layers").
+ * Arithmetic follows the same page's rule for these dots: f32 operands, f32
+ * products and f32 sums (section 2, PAGED_ATTENTION bullet); stored bf16 or fp8
+ * keys and values are widened to f32 exactly before use.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller (e.g. torch CUDA
+ *   tensors), contiguous, in the layouts stated below, and 16-byte aligned.  The
+ *   library allocates nothing, keeps no state between calls and never
+ *   synchronises: every call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *   is the default stream) and returns.
+ * - Pools are updated in place at the addresses given (the pages donate the pool
+ *   buffers to each execution so that the updated pool is written where it was
+ *   read, section 3, "donation pairs").
+ * - Each call returns TL_OK (0) or a negative tl_status.  Argument checks run on the
+ *   host before anything is enqueued; on failure nothing is enqueued and
+ *   tl_last_error() names the offending argument.  Contents of device arrays
+ *   (slot ids, table entries, lengths, positions) are the caller's contract and
+ *   are not read on the host, except when the environment variable TL_VALIDATE=1
+ *   is set: then those arrays are copied to the host (a synchronising copy) and
+ *   range-checked before launch.  Kernels never access memory outside the
+ *   arrays described here, whatever the contents: an out-of-range slot is
+ *   skipped by the write, an out-of-range table entry or length is clamped.
+ * - Supported shapes: head_dim D in {64, 128}; page_size S a power of two with
+ *   8 <= S <= 1024; num_pages * page_size < 2^31; G = num_q_heads / num_kv_heads
+ *   in {1, 2, 4, 8}.  Other shapes return TL_ERR_UNSUPPORTED.
+ *
+ * Pool layout (one layer; K and V are separate arrays, "numBlocks pages of
+ * blockSize tokens, for K and for V", section 3 manifest bullets):
+ *   x        = 16 / bytes(dtype)  elements per 16-byte chunk (f32 4, bf16 8, fp8 16)
+ *   k        [num_pages][num_kv_heads][head_dim / x][page_size][x]   of dtype
+ *   v        [num_pages][num_kv_heads][page_size][head_dim]          of dtype
+ *   k_scale  [num_pages][num_kv_heads][page_size]  f32  (fp8 only, else NULL)
+ *   v_scale  [num_pages][num_kv_heads][page_size]  f32  (fp8 only, else NULL)
+ * Slot s names page s / page_size, offset s % page_size.  Position j of sequence
+ * b lives on page block_tables[b][j / page_size] at offset j % page_size.
+ *
+ * Stored encodings:
+ *   TL_KV_F32       the f32 bits unchanged;
+ *   TL_KV_BF16      round to nearest, ties to even (NaN kept quiet, sign kept);
+ *   TL_KV_FP8_E4M3  OCP e4m3fn codes with one f32 scale per (token, kv head):
+ *                   scale = f32(max_d |x_d| / 448) (1 for an all-zero row),
+ *                   code_d = RNE_e4m3fn(clamp(f32(x_d / scale), -448, 448)),
+ *                   both divisions IEEE f32 (section 6, FP8 and FP8 KV cache
+ *                   paragraphs).  Value = code * scale.
+ */
+#ifndef TL_H
+#define TL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TL_OK = 0,
+  TL_ERR_INVALID = -1,      /* an argument is null, negative, misaligned or inconsistent */
+  TL_ERR_UNSUPPORTED = -2,  /* a shape or dtype outside the supported set above */
+  TL_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace_size query */
+  TL_ERR_HIP = -4           /* a HIP runtime call failed (message in tl_last_error) */
+} tl_status;
+
+typedef enum { TL_KV_F32 = 0, TL_KV_BF16 = 1, TL_KV_FP8_E4M3 = 2 } tl_kv_dtype;
+
+/* One layer's page pool.  The struct itself is a host object read during the call. */
+typedef struct {
+  void* k;         /* device, layout above */
+  void* v;         /* device, layout above */
+  float* k_scale;  /* device, fp8 only */
+  float* v_scale;  /* device, fp8 only */
+  int32_t dtype;   /* tl_kv_dtype */
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+} tl_kv_pool;
+
+/*
+ * KV_CACHE_WRITE ("How serving works in Tlaloc", section 1 decoder graph and
+ * section 2 KV_CACHE_WRITE bullet: a scatter into the pool at the token's slot).
+ *   k_new, v_new  [n_tokens][num_kv_heads][head_dim] f32
+ *   slots         [n_tokens] int32; -1 = pad, never written (section 1, prefill
+ *                 entries).  Slots of one call must be distinct (a repeated slot
+ *                 is a caller error; which row lands is then unspecified).
+ * n_tokens == 0 is a no-op.  Encodes per the pool dtype (see above).
+ */
+int tl_kv_cache_write(const tl_kv_pool* pool, const float* k_new, const float* v_new,
+                      const int32_t* slots, int64_t n_tokens, void* stream);
+
+/*
+ * PAGED_ATTENTION, decode entry ("How serving works in Tlaloc", section 1: one new
+ * token per sequence; section 2: gather the pages the block table names, f32 dots,
+ * masked softmax; section 3: sliding window).  Split-K over the context, then a merge.
+ *   q             [batch][num_q_heads][head_dim] f32, the new token's queries
+ *   block_tables  [batch][max_blocks] int32 page ids; entries past ceil(len/S) unused
+ *   seq_lens      [batch] int32, positions held INCLUDING the new token, whose
+ *                 position is seq_lens[b]-1 (its K/V must already be written);
+ *                 0 gives an all-zero output row
+ *   window        <= 0: full causal attention; W > 0: keys p-W+1 .. p only
+ *   scale         multiplies q.k (e.g. 1/sqrt(head_dim))
+ *   out           [batch][num_q_heads][head_dim] f32
+ *   workspace     device scratch of at least tl_paged_attn_decode_workspace_size(...)
+ *                 bytes (partial softmax states); contents need no initialisation
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * Results depend only on each sequence's own inputs (no cross-sequence reductions),
+ * so a sequence's output is the same bits in any batch.
+ */
+size_t tl_paged_attn_decode_workspace_size(const tl_kv_pool* pool, int32_t batch,
+                                           int32_t num_q_heads, int32_t max_blocks);
+int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                         const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t batch, int32_t window, float scale,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * PAGED_ATTENTION, prefill entry ("How serving works in Tlaloc", section 1: each
+ * sequence has its own right-aligned row of the token axis, pads first; a token's
+ * causal length is its position + 1; section 2 blockwise bullet: online softmax over
+ * 2,048-key blocks from the first block a row can see to the block of its last
+ * position; section 3: chunked prefill over cached history).  Each sequence's pages
+ * are read once per query tile in the kernel, never gathered per token.
+ *   q             [batch][tokens_per_row][num_q_heads][head_dim] f32
+ *   positions     [batch][tokens_per_row] int32; -1 = pad (its output row is 0).
+ *                 Every position's K/V (and all earlier visible ones) must already be
+ *                 written, i.e. call tl_kv_cache_write for the chunk first.
+ *   out           [batch][tokens_per_row][num_q_heads][head_dim] f32 (every row written)
+ *   workspace     may be NULL when tl_paged_attn_prefill_workspace_size(...) is 0
+ */
+size_t tl_paged_attn_prefill_workspace_size(const tl_kv_pool* pool, int32_t batch,
+                                            int32_t tokens_per_row, int32_t num_q_heads,
+                                            int32_t max_blocks);
+int tl_paged_attn_prefill(const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* positions, int32_t batch, int32_t tokens_per_row,
+                          int32_t window, float scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Copy sequence positions 0..length-1 out of the pool in logical order, as stored
+ * (no decoding), so that a test can compare written/gathered KV byte for byte
+ * ("How serving works in Tlaloc", section 2: the pages a block table names).
+ *   block_table_row  [>= ceil(length / page_size)] int32 (device)
+ *   k_out, v_out     [length][num_kv_heads][head_dim] of the pool dtype (device)
+ *   k_scale_out, v_scale_out  [length][num_kv_heads] f32 (fp8 only, else NULL)
+ */
+int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t length,
+                 void* k_out, void* v_out, float* k_scale_out, float* v_scale_out,
+                 void* stream);
+
+/* Message of the last failing call on this thread ("" if none).  Owned by the library. */
+const char* tl_last_error(void);
+
+/* ABI version: 1. */
+int tl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TL_H */

@@ -1,1 +1,225 @@
-"""Paged KV write and paged attention for MI355X (placeholder until the binding lands)."""
+"""Paged KV-cache write and paged attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libtl.so`` (C ABI in ``include/tl.h``).  It only
+marshals arguments: every step of the path runs in the HIP kernels.  torch is
+used for device memory and streams.  The binding has no fallback: if the
+library is missing or its call fails, it raises.
+
+Names follow the C ABI: ``tl_kv_cache_write``, ``tl_paged_attn_decode``,
+``tl_paged_attn_prefill``, ``tl_kv_gather`` and the workspace-size queries.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtl.so")
+
+KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+TL_OK, TL_ERR_INVALID, TL_ERR_UNSUPPORTED, TL_ERR_WORKSPACE, TL_ERR_HIP = 0, -1, -2, -3, -4
+
+
+class TLError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+        self.message = message
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtl.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(_Pool)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.tl_kv_cache_write.argtypes = [P, vp, vp, vp, i64, vp]
+        L.tl_paged_attn_decode_workspace_size.argtypes = [P, i32, i32, i32]
+        L.tl_paged_attn_decode_workspace_size.restype = sz
+        L.tl_paged_attn_decode.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp, sz, vp]
+        L.tl_paged_attn_prefill_workspace_size.argtypes = [P, i32, i32, i32, i32]
+        L.tl_paged_attn_prefill_workspace_size.restype = sz
+        L.tl_paged_attn_prefill.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
+        L.tl_kv_gather.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
+        L.tl_last_error.restype = ctypes.c_char_p
+        L.tl_abi_version.restype = ctypes.c_int
+        for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != TL_OK:
+        raise TLError(rc, lib().tl_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# --------------------------------------------------------------------- pool
+@dataclass
+class KVPool:
+    """One layer's K/V page pool in device memory (layouts of include/tl.h)."""
+
+    k: "object"
+    v: "object"
+    k_scale: "object"
+    v_scale: "object"
+    kv_dtype: str
+    num_pages: int
+    page_size: int
+    num_kv_heads: int
+    head_dim: int
+
+    @property
+    def chunk(self) -> int:
+        """Elements per 16-byte chunk of the K layout."""
+        return 16 // ELEM_BYTES[self.kv_dtype]
+
+    @staticmethod
+    def allocate(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int, kv_dtype: str,
+                 device="cuda", fill_byte: int | None = None) -> "KVPool":
+        import torch
+        x = 16 // ELEM_BYTES[kv_dtype]
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[kv_dtype]
+        kshape = (num_pages, num_kv_heads, head_dim // x, page_size, x)
+        vshape = (num_pages, num_kv_heads, page_size, head_dim)
+        mk = (lambda s, dt: torch.empty(s, dtype=dt, device=device))
+        k, v = mk(kshape, tdt), mk(vshape, tdt)
+        ks = vs = None
+        if kv_dtype == "fp8":
+            ks = mk((num_pages, num_kv_heads, page_size), torch.float32)
+            vs = mk((num_pages, num_kv_heads, page_size), torch.float32)
+        pool = KVPool(k, v, ks, vs, kv_dtype, num_pages, page_size, num_kv_heads, head_dim)
+        if fill_byte is not None:
+            for t in pool.tensors():
+                t.view(torch.uint8).fill_(fill_byte)
+        return pool
+
+    def tensors(self):
+        return [t for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None]
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+    def c_struct(self) -> _Pool:
+        return _Pool(self.k.data_ptr(), self.v.data_ptr(), _ptr(self.k_scale), _ptr(self.v_scale),
+                     KV_DTYPES[self.kv_dtype], self.num_pages, self.page_size, self.num_kv_heads, self.head_dim)
+
+
+# --------------------------------------------------------------- entry points
+def tl_kv_cache_write(pool: KVPool, k_new, v_new, slots, stream=None) -> None:
+    """KV_CACHE_WRITE: k_new/v_new f32 [n, H_kv, D], slots int32 [n] (-1 = skip)."""
+    n = int(slots.numel())
+    ps = pool.c_struct()
+    _check(lib().tl_kv_cache_write(ctypes.byref(ps), k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(), n,
+                                   _stream(stream)))
+
+
+def tl_paged_attn_decode_workspace_size(pool: KVPool, batch: int, num_q_heads: int, max_blocks: int) -> int:
+    ps = pool.c_struct()
+    return int(lib().tl_paged_attn_decode_workspace_size(ctypes.byref(ps), batch, num_q_heads, max_blocks))
+
+
+def tl_paged_attn_prefill_workspace_size(pool: KVPool, batch: int, tokens_per_row: int, num_q_heads: int,
+                                         max_blocks: int) -> int:
+    ps = pool.c_struct()
+    return int(lib().tl_paged_attn_prefill_workspace_size(ctypes.byref(ps), batch, tokens_per_row, num_q_heads,
+                                                          max_blocks))
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def tl_paged_attn_decode(pool: KVPool, q, block_tables, seq_lens, window: int = 0, scale: float | None = None,
+                         out=None, workspace=None, stream=None):
+    """PAGED_ATTENTION decode: q f32 [B, H_q, D]; block_tables int32 [B, max_blocks]; seq_lens int32 [B]."""
+    import torch
+    B, Hq, D = q.shape
+    max_blocks = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = tl_paged_attn_decode_workspace_size(pool, B, Hq, max_blocks)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ps = pool.c_struct()
+    sc = default_scale(D) if scale is None else scale
+    _check(lib().tl_paged_attn_decode(ctypes.byref(ps), q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks,
+                                      seq_lens.data_ptr(), B, window, sc, out.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tl_paged_attn_prefill(pool: KVPool, q, block_tables, positions, window: int = 0, scale: float | None = None,
+                          out=None, workspace=None, stream=None):
+    """PAGED_ATTENTION prefill: q f32 [B, T, H_q, D]; positions int32 [B, T] (-1 = pad)."""
+    import torch
+    B, T, Hq, D = q.shape
+    max_blocks = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ps = pool.c_struct()
+    sc = default_scale(D) if scale is None else scale
+    _check(lib().tl_paged_attn_prefill(ctypes.byref(ps), q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks,
+                                       positions.data_ptr(), B, T, window, sc, out.data_ptr(), ws_ptr, ws_bytes,
+                                       _stream(stream)))
+    return out
+
+
+def tl_kv_gather(pool: KVPool, block_table_row, length: int, stream=None):
+    """Stored rows of positions 0..length-1 in logical order: k, v [L, H_kv, D] (+ scales [L, H_kv])."""
+    import torch
+    dev = pool.k.device
+    shp = (length, pool.num_kv_heads, pool.head_dim)
+    k = torch.empty(shp, dtype=pool.k.dtype, device=dev)
+    v = torch.empty(shp, dtype=pool.v.dtype, device=dev)
+    ks = vs = None
+    if pool.kv_dtype == "fp8":
+        ks = torch.empty((length, pool.num_kv_heads), dtype=torch.float32, device=dev)
+        vs = torch.empty((length, pool.num_kv_heads), dtype=torch.float32, device=dev)
+    ps = pool.c_struct()
+    _check(lib().tl_kv_gather(ctypes.byref(ps), block_table_row.data_ptr(), length, k.data_ptr(), v.data_ptr(),
+                              _ptr(ks), _ptr(vs), _stream(stream)))
+    return k, v, ks, vs
+
+
+def tl_last_error() -> str:
+    return lib().tl_last_error().decode()
+
+
+def tl_abi_version() -> int:
+    return int(lib().tl_abi_version())
+
+
+__all__ = ["KVPool", "TLError", "tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill",
+           "tl_kv_gather", "tl_paged_attn_decode_workspace_size", "tl_paged_attn_prefill_workspace_size",
+           "tl_last_error", "tl_abi_version", "lib"]

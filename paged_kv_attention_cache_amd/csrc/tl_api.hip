@@ -1,0 +1,320 @@
+// C ABI of libtl: argument validation on the host, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation (except the opt-in
+// TL_VALIDATE=1 range checks, which copy index arrays to the host).
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "tl_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return TL_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+bool validate_mode() {
+  const char* e = getenv("TL_VALIDATE");
+  return e && e[0] == '1';
+}
+
+int check_pool(const char* fn, const tl_kv_pool* pool) {
+  if (!pool) return fail(TL_ERR_INVALID, "%s: pool is NULL", fn);
+  if (pool->dtype < TL_KV_F32 || pool->dtype > TL_KV_FP8_E4M3)
+    return fail(TL_ERR_UNSUPPORTED, "%s: pool->dtype (%d) is not a tl_kv_dtype", fn, pool->dtype);
+  if (!pool->k) return fail(TL_ERR_INVALID, "%s: pool->k is NULL", fn);
+  if (!pool->v) return fail(TL_ERR_INVALID, "%s: pool->v is NULL", fn);
+  if (!aligned(pool->k, 16)) return fail(TL_ERR_INVALID, "%s: pool->k is not 16-byte aligned", fn);
+  if (!aligned(pool->v, 16)) return fail(TL_ERR_INVALID, "%s: pool->v is not 16-byte aligned", fn);
+  if (pool->dtype == TL_KV_FP8_E4M3) {
+    if (!pool->k_scale) return fail(TL_ERR_INVALID, "%s: pool->k_scale is NULL for an fp8 pool", fn);
+    if (!pool->v_scale) return fail(TL_ERR_INVALID, "%s: pool->v_scale is NULL for an fp8 pool", fn);
+    if (!aligned(pool->k_scale, 16)) return fail(TL_ERR_INVALID, "%s: pool->k_scale is not 16-byte aligned", fn);
+    if (!aligned(pool->v_scale, 16)) return fail(TL_ERR_INVALID, "%s: pool->v_scale is not 16-byte aligned", fn);
+  }
+  if (pool->num_pages <= 0) return fail(TL_ERR_INVALID, "%s: pool->num_pages (%d) must be > 0", fn, pool->num_pages);
+  if (pool->num_kv_heads <= 0)
+    return fail(TL_ERR_INVALID, "%s: pool->num_kv_heads (%d) must be > 0", fn, pool->num_kv_heads);
+  if (pool->head_dim != 64 && pool->head_dim != 128)
+    return fail(TL_ERR_UNSUPPORTED, "%s: pool->head_dim (%d) must be 64 or 128", fn, pool->head_dim);
+  if (!is_pow2(pool->page_size) || pool->page_size < 8 || pool->page_size > 1024)
+    return fail(TL_ERR_UNSUPPORTED, "%s: pool->page_size (%d) must be a power of two in [8, 1024]", fn,
+                pool->page_size);
+  if ((int64_t)pool->num_pages * pool->page_size >= ((int64_t)1 << 31))
+    return fail(TL_ERR_UNSUPPORTED, "%s: pool->num_pages * pool->page_size must be < 2^31", fn);
+  return TL_OK;
+}
+
+tl::PoolArgs pool_args(const tl_kv_pool* p) {
+  tl::PoolArgs a;
+  a.k = p->k; a.v = p->v; a.k_scale = p->k_scale; a.v_scale = p->v_scale;
+  a.num_pages = p->num_pages; a.page_size = p->page_size; a.page_shift = log2i(p->page_size);
+  a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
+  return a;
+}
+
+int hip_fail(const char* fn, hipError_t e) {
+  return fail(TL_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+template <typename T>
+int copy_to_host(const char* fn, const char* what, const T* src, size_t n, std::vector<T>& dst, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return TL_OK;
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(TL_ERR_HIP, "%s: TL_VALIDATE copy of %s failed (%s)", fn, what, hipGetErrorString(e));
+  return TL_OK;
+}
+
+int check_tables(const char* fn, const tl_kv_pool* pool, const std::vector<int32_t>& tables, int32_t max_blocks,
+                 int32_t b, int64_t positions_needed) {
+  const int64_t blocks = (positions_needed + pool->page_size - 1) / pool->page_size;
+  for (int64_t i = 0; i < blocks; ++i) {
+    const int32_t p = tables[(size_t)b * max_blocks + i];
+    if (p < 0 || p >= pool->num_pages)
+      return fail(TL_ERR_INVALID, "%s: block_tables[%d][%lld] = %d is not a page of the pool (TL_VALIDATE)", fn, b,
+                  (long long)i, p);
+  }
+  return TL_OK;
+}
+
+int check_group(const char* fn, const tl_kv_pool* pool, int32_t num_q_heads) {
+  if (num_q_heads <= 0) return fail(TL_ERR_INVALID, "%s: num_q_heads (%d) must be > 0", fn, num_q_heads);
+  if (num_q_heads % pool->num_kv_heads != 0)
+    return fail(TL_ERR_INVALID, "%s: num_q_heads (%d) is not a multiple of pool->num_kv_heads (%d)", fn, num_q_heads,
+                pool->num_kv_heads);
+  const int g = num_q_heads / pool->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(TL_ERR_UNSUPPORTED, "%s: num_q_heads / num_kv_heads (%d) must be 1, 2, 4 or 8", fn, g);
+  return TL_OK;
+}
+
+int64_t decode_nsplit(const tl_kv_pool* pool, int32_t num_q_heads, int32_t max_blocks) {
+  const int sk = tl::decode_split_keys(pool->dtype, num_q_heads / pool->num_kv_heads, pool->page_size);
+  const int64_t keys = (int64_t)max_blocks * pool->page_size;
+  return (keys + sk - 1) / sk;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tl_last_error(void) { return g_err; }
+
+int tl_abi_version(void) { return 1; }
+
+int tl_kv_cache_write(const tl_kv_pool* pool, const float* k_new, const float* v_new, const int32_t* slots,
+                      int64_t n_tokens, void* stream) {
+  const char* fn = "tl_kv_cache_write";
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(TL_ERR_INVALID, "%s: n_tokens (%lld) must be >= 0", fn, (long long)n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!k_new) return fail(TL_ERR_INVALID, "%s: k_new is NULL", fn);
+  if (!v_new) return fail(TL_ERR_INVALID, "%s: v_new is NULL", fn);
+  if (!slots) return fail(TL_ERR_INVALID, "%s: slots is NULL", fn);
+  if (!aligned(k_new, 16)) return fail(TL_ERR_INVALID, "%s: k_new is not 16-byte aligned", fn);
+  if (!aligned(v_new, 16)) return fail(TL_ERR_INVALID, "%s: v_new is not 16-byte aligned", fn);
+  if (!aligned(slots, 4)) return fail(TL_ERR_INVALID, "%s: slots is not 4-byte aligned", fn);
+  if (n_tokens * pool->num_kv_heads >= ((int64_t)1 << 31) / 8)
+    return fail(TL_ERR_UNSUPPORTED, "%s: n_tokens * num_kv_heads is too large for one call", fn);
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> h;
+    if ((rc = copy_to_host(fn, "slots", slots, (size_t)n_tokens, h, s))) return rc;
+    const int64_t limit = (int64_t)pool->num_pages * pool->page_size;
+    std::vector<int32_t> live;
+    for (int64_t i = 0; i < n_tokens; ++i) {
+      if (h[i] == -1) continue;
+      if (h[i] < 0 || h[i] >= limit)
+        return fail(TL_ERR_INVALID, "%s: slots[%lld] = %d is outside the pool (TL_VALIDATE)", fn, (long long)i, h[i]);
+      live.push_back(h[i]);
+    }
+    std::sort(live.begin(), live.end());
+    for (size_t i = 1; i < live.size(); ++i)
+      if (live[i] == live[i - 1]) return fail(TL_ERR_INVALID, "%s: slot %d appears twice (TL_VALIDATE)", fn, live[i]);
+  }
+  tl::WriteArgs a;
+  a.pool = pool_args(pool);
+  a.k = pool->k; a.v = pool->v; a.k_scale = pool->k_scale; a.v_scale = pool->v_scale;
+  a.k_new = k_new; a.v_new = v_new; a.slots = slots; a.n_tokens = n_tokens;
+  hipError_t e = tl::launch_write(a, pool->dtype, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+size_t tl_paged_attn_decode_workspace_size(const tl_kv_pool* pool, int32_t batch, int32_t num_q_heads,
+                                           int32_t max_blocks) {
+  const char* fn = "tl_paged_attn_decode_workspace_size";
+  if (check_pool(fn, pool) || check_group(fn, pool, num_q_heads)) return 0;
+  if (batch <= 0 || max_blocks <= 0) return 0;
+  const int64_t ns = decode_nsplit(pool, num_q_heads, max_blocks);
+  return (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float);
+}
+
+int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t window, float scale,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tl_paged_attn_decode";
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if (batch > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: batch (%d) must be <= 65535", fn, batch);
+  if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
+  if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
+    return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
+  if (batch == 0) return ok();
+  if (!q) return fail(TL_ERR_INVALID, "%s: q is NULL", fn);
+  if (!out) return fail(TL_ERR_INVALID, "%s: out is NULL", fn);
+  if (!block_tables) return fail(TL_ERR_INVALID, "%s: block_tables is NULL", fn);
+  if (!seq_lens) return fail(TL_ERR_INVALID, "%s: seq_lens is NULL", fn);
+  if (!aligned(q, 16)) return fail(TL_ERR_INVALID, "%s: q is not 16-byte aligned", fn);
+  if (!aligned(out, 16)) return fail(TL_ERR_INVALID, "%s: out is not 16-byte aligned", fn);
+  if (!aligned(block_tables, 4)) return fail(TL_ERR_INVALID, "%s: block_tables is not 4-byte aligned", fn);
+  if (!aligned(seq_lens, 4)) return fail(TL_ERR_INVALID, "%s: seq_lens is not 4-byte aligned", fn);
+  const size_t need = tl_paged_attn_decode_workspace_size(pool, batch, num_q_heads, max_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(TL_ERR_WORKSPACE, "%s: workspace (%zu bytes) is smaller than the %zu bytes required", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (!aligned(workspace, 16)) return fail(TL_ERR_INVALID, "%s: workspace is not 16-byte aligned", fn);
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> lens, tables;
+    if ((rc = copy_to_host(fn, "seq_lens", seq_lens, (size_t)batch, lens, s))) return rc;
+    if ((rc = copy_to_host(fn, "block_tables", block_tables, (size_t)batch * max_blocks, tables, s))) return rc;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (lens[b] < 0 || (int64_t)lens[b] > (int64_t)max_blocks * pool->page_size)
+        return fail(TL_ERR_INVALID, "%s: seq_lens[%d] = %d is outside [0, max_blocks * page_size] (TL_VALIDATE)", fn,
+                    b, lens[b]);
+      if ((rc = check_tables(fn, pool, tables, max_blocks, b, lens[b]))) return rc;
+    }
+  }
+  tl::DecodeArgs a;
+  a.pool = pool_args(pool);
+  a.q = q; a.block_tables = block_tables; a.seq_lens = seq_lens; a.out = out;
+  const int64_t ns = decode_nsplit(pool, num_q_heads, max_blocks);
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = a.ws_acc + (size_t)batch * num_q_heads * ns * pool->head_dim;
+  a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = max_blocks;
+  a.batch = batch; a.window = window;
+  a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->page_size);
+  a.n_split = (int)ns;
+  a.qscale = scale * tl::LOG2E;
+  hipError_t e = tl::launch_decode(a, pool->dtype, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+size_t tl_paged_attn_prefill_workspace_size(const tl_kv_pool* pool, int32_t batch, int32_t tokens_per_row,
+                                            int32_t num_q_heads, int32_t max_blocks) {
+  (void)pool; (void)batch; (void)tokens_per_row; (void)num_q_heads; (void)max_blocks;
+  return 0;
+}
+
+int tl_paged_attn_prefill(const tl_kv_pool* pool, const float* q, int32_t num_q_heads, const int32_t* block_tables,
+                          int32_t max_blocks, const int32_t* positions, int32_t batch, int32_t tokens_per_row,
+                          int32_t window, float scale, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const char* fn = "tl_paged_attn_prefill";
+  (void)workspace; (void)workspace_bytes;
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if (batch > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: batch (%d) must be <= 65535", fn, batch);
+  if (tokens_per_row < 0) return fail(TL_ERR_INVALID, "%s: tokens_per_row (%d) must be >= 0", fn, tokens_per_row);
+  if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
+  if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
+    return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
+  if ((int64_t)batch * tokens_per_row * num_q_heads >= ((int64_t)1 << 31) / 128)
+    return fail(TL_ERR_UNSUPPORTED, "%s: batch * tokens_per_row * num_q_heads is too large for one call", fn);
+  if (batch == 0 || tokens_per_row == 0) return ok();
+  if (!q) return fail(TL_ERR_INVALID, "%s: q is NULL", fn);
+  if (!out) return fail(TL_ERR_INVALID, "%s: out is NULL", fn);
+  if (!block_tables) return fail(TL_ERR_INVALID, "%s: block_tables is NULL", fn);
+  if (!positions) return fail(TL_ERR_INVALID, "%s: positions is NULL", fn);
+  if (!aligned(q, 16)) return fail(TL_ERR_INVALID, "%s: q is not 16-byte aligned", fn);
+  if (!aligned(out, 16)) return fail(TL_ERR_INVALID, "%s: out is not 16-byte aligned", fn);
+  if (!aligned(block_tables, 4)) return fail(TL_ERR_INVALID, "%s: block_tables is not 4-byte aligned", fn);
+  if (!aligned(positions, 4)) return fail(TL_ERR_INVALID, "%s: positions is not 4-byte aligned", fn);
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> pos, tables;
+    if ((rc = copy_to_host(fn, "positions", positions, (size_t)batch * tokens_per_row, pos, s))) return rc;
+    if ((rc = copy_to_host(fn, "block_tables", block_tables, (size_t)batch * max_blocks, tables, s))) return rc;
+    for (int32_t b = 0; b < batch; ++b) {
+      int64_t pmax = -1;
+      for (int32_t t = 0; t < tokens_per_row; ++t) {
+        const int32_t p = pos[(size_t)b * tokens_per_row + t];
+        if (p < -1 || (int64_t)p >= (int64_t)max_blocks * pool->page_size)
+          return fail(TL_ERR_INVALID, "%s: positions[%d][%d] = %d is outside [-1, max_blocks * page_size) (TL_VALIDATE)",
+                      fn, b, t, p);
+        pmax = std::max<int64_t>(pmax, p);
+      }
+      if ((rc = check_tables(fn, pool, tables, max_blocks, b, pmax + 1))) return rc;
+    }
+  }
+  tl::PrefillArgs a;
+  a.pool = pool_args(pool);
+  a.q = q; a.block_tables = block_tables; a.positions = positions; a.out = out;
+  a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = max_blocks;
+  a.batch = batch; a.tokens_per_row = tokens_per_row; a.window = window;
+  a.tokens_per_wg = tl::prefill_tokens_per_wg(a.group);
+  a.n_qtiles = (tokens_per_row + a.tokens_per_wg - 1) / a.tokens_per_wg;
+  a.qscale = scale * tl::LOG2E;
+  hipError_t e = tl::launch_prefill(a, pool->dtype, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t length, void* k_out, void* v_out,
+                 float* k_scale_out, float* v_scale_out, void* stream) {
+  const char* fn = "tl_kv_gather";
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if (length < 0) return fail(TL_ERR_INVALID, "%s: length (%d) must be >= 0", fn, length);
+  if (length == 0) return ok();
+  if (!block_table_row) return fail(TL_ERR_INVALID, "%s: block_table_row is NULL", fn);
+  if (!k_out) return fail(TL_ERR_INVALID, "%s: k_out is NULL", fn);
+  if (!v_out) return fail(TL_ERR_INVALID, "%s: v_out is NULL", fn);
+  if (!aligned(k_out, 16) || !aligned(v_out, 16)) return fail(TL_ERR_INVALID, "%s: k_out/v_out not 16-byte aligned", fn);
+  if (pool->dtype == TL_KV_FP8_E4M3 && (!k_scale_out || !v_scale_out))
+    return fail(TL_ERR_INVALID, "%s: k_scale_out/v_scale_out are NULL for an fp8 pool", fn);
+  hipStream_t s = (hipStream_t)stream;
+  tl::GatherArgs a;
+  a.pool = pool_args(pool);
+  a.table = block_table_row; a.length = length;
+  a.k_out = k_out; a.v_out = v_out; a.k_scale_out = k_scale_out; a.v_scale_out = v_scale_out;
+  hipError_t e = tl::launch_gather(a, pool->dtype, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Internal declarations of libtl: device helpers shared by the kernels and the
+// host launchers that tl_api.hip calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tl.h"
+
+namespace tl {
+
+// ------------------------------------------------------------ vector types
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+template <int KVT> struct KvTraits;
+template <> struct KvTraits<KV_F32> { typedef float T; static constexpr int BYTES = 4; static constexpr int X = 4; };
+template <> struct KvTraits<KV_BF16> { typedef uint16_t T; static constexpr int BYTES = 2; static constexpr int X = 8; };
+template <> struct KvTraits<KV_FP8> { typedef uint8_t T; static constexpr int BYTES = 1; static constexpr int X = 16; };
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int KEY_BLOCK = 2048;  // the pages' key-block width; loop bounds are taken per block
+
+// ----------------------------------------------------------- conversions
+// bf16 bits -> f32: the bf16 pattern is the top half of the f32 pattern (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN with its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// four fp8 e4m3fn codes packed in a dword -> four f32 (hardware convert, exact)
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+}
+
+// widen one 16-byte chunk of stored elements to f32 (X values)
+template <int KVT>
+__device__ __forceinline__ void widen_chunk(const uint4& c, float* o) {
+  if constexpr (KVT == KV_F32) {
+    o[0] = __uint_as_float(c.x); o[1] = __uint_as_float(c.y);
+    o[2] = __uint_as_float(c.z); o[3] = __uint_as_float(c.w);
+  } else if constexpr (KVT == KV_BF16) {
+    o[0] = bf16_lo(c.x); o[1] = bf16_hi(c.x); o[2] = bf16_lo(c.y); o[3] = bf16_hi(c.y);
+    o[4] = bf16_lo(c.z); o[5] = bf16_hi(c.z); o[6] = bf16_lo(c.w); o[7] = bf16_hi(c.w);
+  } else {
+    fp8x4_to_f32(c.x, o); fp8x4_to_f32(c.y, o + 4); fp8x4_to_f32(c.z, o + 8); fp8x4_to_f32(c.w, o + 12);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// broadcast lane (lane & ~3) | R of each quad to the whole quad (DPP quad_perm)
+template <int R>
+__device__ __forceinline__ float quad_bcast(float v) {
+  constexpr int ctrl = R | (R << 2) | (R << 4) | (R << 6);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+__device__ __forceinline__ float wave_xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
+
+// ------------------------------------------------------------ launch args
+struct PoolArgs {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  int num_pages, page_size, page_shift, num_kv_heads, head_dim;
+};
+
+struct WriteArgs {
+  PoolArgs pool;
+  void* k;  // writable aliases of pool.k / pool.v / scales
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  const float* k_new;
+  const float* v_new;
+  const int32_t* slots;
+  int64_t n_tokens;
+};
+
+struct GatherArgs {
+  PoolArgs pool;
+  const int32_t* table;
+  int length;
+  void* k_out;
+  void* v_out;
+  float* k_scale_out;
+  float* v_scale_out;
+};
+
+struct DecodeArgs {
+  PoolArgs pool;
+  const float* q;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* out;
+  float* ws_acc;   // [batch][num_q_heads][n_split][head_dim]
+  float* ws_ml;    // [batch][num_q_heads][n_split][2]
+  int num_q_heads, group, max_blocks, batch, window, split_keys, n_split;
+  float qscale;    // scale * log2(e): scores come out in log2 units
+};
+
+struct PrefillArgs {
+  PoolArgs pool;
+  const float* q;
+  const int32_t* block_tables;
+  const int32_t* positions;
+  float* out;
+  int num_q_heads, group, max_blocks, batch, tokens_per_row, window, n_qtiles, tokens_per_wg;
+  float qscale;
+};
+
+// ------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are already validated.
+hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int kv_dtype, hipStream_t s);
+int decode_split_keys(int kv_dtype, int group, int page_size);
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s);
+int prefill_tokens_per_wg(int group);
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t s);
+
+}  // namespace tl

@@ -87,7 +87,7 @@ class Workload:
 
     def history_len(self, b: int) -> int:
         if self.kind == "decode":
-            return int(self.seq_lens[b]) - 1
+            return max(0, int(self.seq_lens[b]) - 1)
         return int(self.start_pos[b])
 
     # --------------------------------------------------------------- streams
@@ -150,6 +150,10 @@ class Workload:
         ks, vs, ss = [], [], []
         for b in range(self.batch):
             L = int(self.seq_lens[b])
+            if L == 0:  # nothing to write: a pad row
+                z = np.zeros((self.num_kv_heads, self.head_dim), np.float32)
+                ks.append(z); vs.append(z); ss.append(-1)
+                continue
             k, v = self.seq_kv(b)
             ks.append(k[L - 1]); vs.append(v[L - 1])
             ss.append(self.slots_for(b, np.array([L - 1]))[0])

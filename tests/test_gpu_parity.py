@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Writes and gathered KV: byte for byte, whole pools including untouched sentinel
+pages and scale arrays.  Attention outputs: worst per-row error
+max_d|o - o_ref| / max_d|o_ref| <= 2e-5 (f32 and bf16 KV) or 1e-2 (fp8 KV against
+the dequantised oracle); rows with no visible key must be exactly 0.
+Full-size configurations are checked on sampled sequences/tokens, which the
+oracle recomputes from a contiguous copy of the sequence's stored history.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import encode as E
+from paged_kv_attention_cache_amd import workloads as W
+from paged_kv_attention_cache_amd import runner as R
+from tests.helpers import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-5, "bf16": 2e-5, "fp8": 1e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests need an MI355X")
+    import paged_kv_attention_cache_amd as tl
+    tl.lib()  # raises if libtl.so is missing
+    return torch
+
+
+def oracle_pool_for(wl, history=True, step=True):
+    pool = oracle.KVPool(wl.num_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, sentinel=R.SENTINEL)
+    if history:
+        for k, v, s in wl.history_batches():
+            pool.write(k, v, s)
+    if step and wl.kind == "decode":
+        pool.write(*wl.decode_step_rows())
+    return pool
+
+
+def assert_pool_equal(gpu_pool, opool):
+    kk, vv, ks, vs = R.pool_logical(gpu_pool)
+    assert np.array_equal(kk.view(np.uint8), opool.k.view(np.uint8)), "K pool bytes differ"
+    assert np.array_equal(vv.view(np.uint8), opool.v.view(np.uint8)), "V pool bytes differ"
+    if ks is not None:
+        assert np.array_equal(ks.view(np.uint32), opool.k_scale.view(np.uint32)), "K scales differ"
+        assert np.array_equal(vs.view(np.uint32), opool.v_scale.view(np.uint32)), "V scales differ"
+
+
+# ====================================================================== writes
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_write_bit_exact_with_sentinels(torch_cuda, kv_dtype, D):
+    torch = torch_cuda
+    P, S, H, n = 6, 16, 2, 70
+    rng = np.random.default_rng(21)
+    k = (rng.standard_normal((n, H, D)) * rng.uniform(0.01, 100, (n, H, 1))).astype(np.float32)
+    v = (rng.standard_normal((n, H, D)) * rng.uniform(0.01, 100, (n, H, 1))).astype(np.float32)
+    k[3, 1] = 0.0  # an all-zero row (fp8 scale 1)
+    slots = rng.permutation(P * S)[:n].astype(np.int32)
+    slots[::7] = -1
+    op = oracle.KVPool(P, S, H, D, kv_dtype, sentinel=R.SENTINEL)
+    op.write(k, v, slots)
+    import paged_kv_attention_cache_amd as tl
+    gp = tl.KVPool.allocate(P, S, H, D, kv_dtype, fill_byte=R.SENTINEL)
+    tl.tl_kv_cache_write(gp, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert_pool_equal(gp, op)
+
+
+def test_fp8_write_codes_match_oracle_at_every_midpoint(torch_cuda):
+    """Rows whose absmax is 448 have scale 1, so the codes are RNE(x) of the inputs themselves."""
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    pos = E.FP8_E4M3FN[:0x7F]
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    vals = np.concatenate([pos.astype(np.float32), mid, np.nextafter(mid, np.float32(np.inf)),
+                           np.nextafter(mid, np.float32(-np.inf)),
+                           np.random.default_rng(5).uniform(-448, 448, 20000).astype(np.float32)])
+    vals = np.concatenate([vals, -vals])
+    vals = np.clip(vals, -448, 448)
+    D = 128
+    per_row = D - 1
+    nrows = (len(vals) + per_row - 1) // per_row
+    x = np.zeros((nrows, per_row), np.float32)
+    x.reshape(-1)[:len(vals)] = vals
+    rows = np.concatenate([np.full((nrows, 1), 448.0, np.float32), x], axis=1)  # absmax 448 -> scale 1
+    H = 1
+    n = nrows
+    S = 16
+    P = (n + S - 1) // S
+    k = rows.reshape(n, H, D)
+    gp = tl.KVPool.allocate(P, S, H, D, "fp8", fill_byte=0)
+    slots = np.arange(n, dtype=np.int32)
+    tl.tl_kv_cache_write(gp, torch.from_numpy(k).cuda(), torch.from_numpy(k).cuda(), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kk, _, ks, _ = R.pool_logical(gp)
+    got = kk.reshape(P * S, H, D)[:n].reshape(n, D)
+    assert np.all(ks.reshape(-1)[:n] == 1.0)
+    want = E.fp8_code(rows)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_write_matches_oracle_on_tie_strata(torch_cuda):
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    hi = np.arange(0, 1 << 16, 7, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    bits = (hi[:, None] | lows[None, :]).reshape(-1)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    D = 128
+    n = len(x) // D
+    x = x[:n * D].reshape(n, 1, D)
+    S = 16
+    P = (n + S - 1) // S
+    gp = tl.KVPool.allocate(P, S, 1, D, "bf16", fill_byte=0)
+    t = torch.from_numpy(x.copy()).cuda()
+    tl.tl_kv_cache_write(gp, t, t, torch.arange(n, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    kk, vv, _, _ = R.pool_logical(gp)
+    want = E.bf16_bits(x.reshape(n, D))
+    assert np.array_equal(kk.reshape(P * S, D)[:n], want)
+    assert np.array_equal(vv.reshape(P * S, D)[:n], want)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_gather_bit_exact(torch_cuda, kv_dtype):
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    wl = W.custom_decode(301, [1, 33, 70], 8, 2, 128, 16, kv_dtype, spare_pages=2)
+    op = oracle_pool_for(wl)
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.DecodeStep(wl, gp)
+    st.write()
+    for b in range(wl.batch):
+        L = int(wl.seq_lens[b])
+        k, v, ks, vs = tl.tl_kv_gather(gp, st.tables[b], L)
+        torch.cuda.synchronize()
+        ok, ov, oks, ovs = op.gather_raw(wl.block_tables[b], L)
+        assert np.array_equal(k.cpu().view(torch.uint8).numpy().reshape(-1), ok.view(np.uint8).reshape(-1))
+        assert np.array_equal(v.cpu().view(torch.uint8).numpy().reshape(-1), ov.view(np.uint8).reshape(-1))
+        if kv_dtype == "fp8":
+            assert np.array_equal(ks.cpu().numpy(), oks) and np.array_equal(vs.cpu().numpy(), ovs)
+
+
+# ====================================================================== decode
+DECODE_CASES = [
+    # (name, lens, Hq, Hkv, D, S, dtype, window)
+    ("g4_bf16_edges", [1, 2, 31, 32, 33, 100], 8, 2, 128, 16, "bf16", 0),
+    ("g8_fp8_split_edges", [511, 512, 513, 1023, 1024, 1025, 2049], 16, 2, 128, 64, "fp8", 0),
+    ("g2_f32_d64", [5, 37, 64, 65], 4, 2, 64, 16, "f32", 0),
+    ("g1_bf16_d64", [300, 1500, 17], 8, 8, 64, 32, "bf16", 0),
+    ("g4_bf16_window", [3000, 700, 64, 1], 8, 2, 128, 16, "bf16", 1000),
+    ("g8_fp8_window", [5000, 2047, 2048, 2049], 16, 2, 128, 64, "fp8", 1100),
+    ("g4_f32_d128", [40, 600, 1], 8, 2, 128, 8, "f32", 0),
+    ("g8_bf16_odd_heads", [77, 1200], 24, 3, 128, 16, "bf16", 0),
+    ("g4_fp8_d64", [129, 1030], 12, 3, 64, 16, "fp8", 0),
+    ("zero_length", [0, 5, 0, 1], 8, 2, 128, 16, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_parity(torch_cuda, case):
+    torch = torch_cuda
+    name, lens, Hq, Hkv, D, S, dt, win = case
+    wl = W.custom_decode(400 + DECODE_CASES.index(case), lens, Hq, Hkv, D, S, dt, window=win, spare_pages=3)
+    op = oracle_pool_for(wl)
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.DecodeStep(wl, gp)
+    out = st.run()
+    torch.cuda.synchronize()
+    assert_pool_equal(gp, op)
+    ref = oracle.decode(op, wl.decode_q(), wl.block_tables, wl.seq_lens, win, wl.scale)
+    got = out.cpu().numpy()
+    err = row_rel_err(got, ref)
+    assert err <= TOL[dt], f"{name}: max row error {err:.3e}"
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[b] == 0)
+
+
+def test_c1_tiny_decode(torch_cuda):
+    torch = torch_cuda
+    wl = W.make("c1")
+    op = oracle_pool_for(wl)
+    gp = R.make_pool(wl)
+    assert R.write_history(gp, wl) == 4 + 36
+    st = R.DecodeStep(wl, gp)
+    out = st.run()
+    torch.cuda.synchronize()
+    assert_pool_equal(gp, op)  # includes the 4 sentinel-filled spare pages
+    ref = oracle.decode(op, wl.decode_q(), wl.block_tables, wl.seq_lens, 0, wl.scale)
+    assert row_rel_err(out.cpu().numpy(), ref) <= 2e-5
+
+
+def test_decode_batch_invariance_bitwise(torch_cuda):
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    wl = W.custom_decode(430, [1500, 77, 3000, 515], 16, 2, 128, 16, "bf16")
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.DecodeStep(wl, gp)
+    full = st.run().clone()
+    for b in range(wl.batch):
+        one = tl.tl_paged_attn_decode(gp, st.q[b:b + 1].contiguous(), st.tables[b:b + 1].contiguous(),
+                                      st.seq_lens[b:b + 1].contiguous(), 0, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], full[b]), f"sequence {b} differs alone vs in batch"
+
+
+# ===================================================================== prefill
+PREFILL_CASES = [
+    # (name, row_lens, start_pos, T, Hq, Hkv, D, S, dtype, window)
+    ("g4_bf16_ragged_pads", [1, 37, 64, 0], [0, 0, 0, 0], 64, 8, 2, 128, 16, "bf16", 0),
+    ("g4_bf16_history", [50, 64], [100, 7], 64, 8, 2, 128, 16, "bf16", 0),
+    ("g4_bf16_window", [64, 40], [300, 0], 64, 8, 2, 128, 16, "bf16", 50),
+    ("g8_bf16", [33, 3], [10, 0], 40, 16, 2, 128, 16, "bf16", 0),
+    ("g1_f32_d64", [70, 5], [0, 60], 70, 4, 4, 64, 16, "f32", 0),
+    ("g2_fp8", [45], [17], 48, 4, 2, 128, 64, "fp8", 0),
+    ("block_boundary", [100, 100], [2000, 1990], 100, 8, 2, 128, 16, "bf16", 0),
+    ("window_crosses_block", [100], [2030], 100, 8, 2, 128, 16, "bf16", 60),
+    ("window_longer_than_context", [30], [5], 32, 8, 2, 128, 16, "bf16", 5000),
+    ("g4_d64_window1", [20], [3], 20, 8, 2, 64, 8, "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_parity(torch_cuda, case):
+    torch = torch_cuda
+    name, rl, sp, T, Hq, Hkv, D, S, dt, win = case
+    wl = W.custom_prefill(500 + PREFILL_CASES.index(case), rl, sp, T, Hq, Hkv, D, S, dt, window=win, spare_pages=2)
+    op = oracle_pool_for(wl)
+    q, k, v, s, pos = wl.prefill_inputs()
+    op.write(k.reshape(-1, Hkv, D), v.reshape(-1, Hkv, D), s.reshape(-1))
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.PrefillStep(wl, gp)
+    out = st.run()
+    torch.cuda.synchronize()
+    assert_pool_equal(gp, op)
+    ref = oracle.prefill(op, q, wl.block_tables, pos, win, wl.scale)
+    got = out.cpu().numpy()
+    err = row_rel_err(got, ref)
+    assert err <= TOL[dt], f"{name}: max row error {err:.3e}"
+    assert np.all(got[pos < 0] == 0)
+
+
+def test_prefill_batch_invariance_and_decode_agreement(torch_cuda):
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    wl = W.custom_prefill(560, [40, 64, 9], [0, 0, 0], 64, 8, 2, 128, 16, "bf16")
+    gp = R.make_pool(wl)
+    st = R.PrefillStep(wl, gp)
+    full = st.run().clone()
+    for b in range(wl.batch):
+        one = tl.tl_paged_attn_prefill(gp, st.q[b:b + 1].contiguous(), st.tables[b:b + 1].contiguous(),
+                                       st.positions[b:b + 1].contiguous(), 0, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], full[b]), f"row {b} differs alone vs in batch"
+    # decode of the last token of each row equals that prefill row (different kernels: tolerance)
+    lens = wl.row_lens.astype(np.int32)
+    q_last = st.q[:, -1].contiguous()
+    dec = tl.tl_paged_attn_decode(gp, q_last, st.tables, torch.from_numpy(lens).cuda(), 0, wl.scale)
+    torch.cuda.synchronize()
+    assert row_rel_err(dec.cpu().numpy(), full[:, -1].cpu().numpy()) <= 2e-5
+
+
+# ============================================================ full-size configs
+def _stored_values(wl, b):
+    k, v = wl.seq_kv(b)
+    kr, ks = E.encode_kv(k, wl.kv_dtype)
+    vr, vs = E.encode_kv(v, wl.kv_dtype)
+    return (kr, ks, vr, vs), E.kv_values(kr, ks, wl.kv_dtype), E.kv_values(vr, vs, wl.kv_dtype)
+
+
+def _check_seq_written(tl, torch, wl, gp, tables, b):
+    L = wl.context_len(b)
+    (kr, ks, vr, vs), _, _ = _stored_values(wl, b)
+    gk, gv, gks, gvs = tl.tl_kv_gather(gp, tables[b], L)
+    torch.cuda.synchronize()
+    assert np.array_equal(gk.cpu().view(torch.uint8).numpy().reshape(-1), kr.view(np.uint8).reshape(-1))
+    assert np.array_equal(gv.cpu().view(torch.uint8).numpy().reshape(-1), vr.view(np.uint8).reshape(-1))
+    if ks is not None:
+        assert np.array_equal(gks.cpu().numpy(), ks) and np.array_equal(gvs.cpu().numpy(), vs)
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c5"])
+def test_full_decode_config_sampled(torch_cuda, cfg):
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    wl = W.make(cfg)
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.DecodeStep(wl, gp)
+    out = st.run().cpu().numpy()
+    L = wl.seq_lens
+    picks = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, wl.batch - 1, wl.batch // 2})
+    q = wl.decode_q()
+    for b in picks:
+        _check_seq_written(tl, torch, wl, gp, st.tables, b)
+        _, Kv, Vv = _stored_values(wl, b)
+        ref = oracle.paged.attend_history(q[b:b + 1], Kv, Vv, np.array([L[b] - 1]), 0, wl.scale)
+        err = row_rel_err(out[b:b + 1], ref)
+        assert err <= TOL[wl.kv_dtype], f"{cfg} seq {b} (L={L[b]}): {err:.3e}"
+    assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("cfg", ["c3", "c4", "c4w"])
+def test_full_prefill_config_sampled(torch_cuda, cfg):
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    wl = W.make(cfg)
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.PrefillStep(wl, gp)
+    out = st.run().cpu().numpy()
+    pos = wl.row_positions()
+    T = wl.tokens_per_row
+    rng = np.random.default_rng(77)
+    for b in range(wl.batch):
+        _check_seq_written(tl, torch, wl, gp, st.tables, b)
+        live = np.nonzero(pos[b] >= 0)[0]
+        pads = np.nonzero(pos[b] < 0)[0]
+        assert np.all(out[b, pads] == 0)
+        ts = np.unique(np.concatenate([live[:3], live[-3:], rng.choice(live, size=min(10, len(live)), replace=False)]))
+        _, Kv, Vv = _stored_values(wl, b)
+        q = wl.prefill_rows(b)[0]
+        ref = oracle.paged.attend_history(q[ts], Kv, Vv, pos[b, ts], wl.window, wl.scale)
+        err = row_rel_err(out[b, ts], ref)
+        assert err <= TOL[wl.kv_dtype], f"{cfg} row {b}: {err:.3e}"
+    assert np.all(np.isfinite(out))
