@@ -16,7 +16,8 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtl.so")
+# TL_LIBRARY may point at another build of the same ABI (e.g. a tuning variant)
+LIB_PATH = os.environ.get("TL_LIBRARY") or os.path.join(HERE, "libtl.so")
 
 KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}

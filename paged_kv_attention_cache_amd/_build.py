@@ -35,14 +35,16 @@ def _run(cmd):
     return p
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str | None = None, build_dir: str | None = None) -> str:
     """Compile every source for gfx950 and link libtl.so next to this file."""
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = build_dir or BUILD
+    lib = out or LIB
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
     objs = []
 
     def one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [cc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
@@ -51,10 +53,10 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
