@@ -145,7 +145,135 @@ def cpu_baseline(seqs: int = 6):
             "seconds": dt}
 
 
+# ------------------------------------------------------------------ rocprofv3 summaries
+# These modes make no GPU call except --copy-calibration; they turn the CSV output of
+# rocprofv3 runs of this file into the short text summaries kept under profiles/.
+
+ATTN_KERNELS = ("decode_split_kernel", "decode_merge_kernel", "decode_prep_kernel", "prefill_kernel")
+
+
+def _short_name(name: str) -> str:
+    for k in ATTN_KERNELS + ("write_kernel", "gather_kernel"):
+        if k in name:
+            return name[name.index(k):].split("(tl::")[0]
+    return name[:60]
+
+
+def _find_csv(d: str, suffix: str) -> str:
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _counter_means(d: str, counter: str):
+    """Mean counter value (KiB) and dispatch count per kernel name in one --pmc run."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(_find_csv(d, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def copy_calibration(gib: int = 1, reps: int = 3):
+    """A plain device-to-device copy of known size, run under rocprofv3 --pmc to scale
+    FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    n = gib << 28
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def traffic_summary(cfg: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                    command: str):
+    """Scale FETCH_SIZE / WRITE_SIZE of the attention kernels by the copy calibration and
+    record bytes per attention call in profiles/traffic.json (keyed by workload)."""
+    copy_bytes = 1 << 30
+    cf = max(v[0] for v in _counter_means(copy_fetch_dir, "FETCH_SIZE").values()) * 1024
+    cw = max(v[0] for v in _counter_means(copy_write_dir, "WRITE_SIZE").values()) * 1024
+    f_fetch, f_write = copy_bytes / cf, copy_bytes / cw
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    lines = [f"# HBM traffic per attention call, workload {cfg}", "",
+             f"command (FETCH_SIZE, then again with WRITE_SIZE): {command}",
+             f"calibration: a 1 GiB device copy (python bench.py --copy-calibration under the same "
+             f"rocprofv3 --pmc) reads {cf / 1024:.0f} KiB and writes {cw / 1024:.0f} KiB per dispatch -> "
+             f"FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | written bytes (scaled) |",
+             "|---|---|---|---|---|---|"]
+    total_r = total_w = 0.0
+    for name in sorted(fetch):
+        short = _short_name(name)
+        if not any(k in name for k in ATTN_KERNELS):
+            continue
+        fr, n = fetch[name]
+        wr = write.get(name, (0.0, 0))[0]
+        rb, wb = fr * 1024 * f_fetch, wr * 1024 * f_write
+        total_r += rb
+        total_w += wb
+        lines.append(f"| {short} | {n} | {fr:.0f} | {wr:.0f} | {rb / 1e9:.4f} GB | {wb / 1e9:.4f} GB |")
+    lines.append(f"| attention call total | | | | {total_r / 1e9:.4f} GB | {total_w / 1e9:.4f} GB |")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec[cfg] = {"source_hash": kernel_source_hash(), "bytes_per_launch": total_r + total_w,
+                "read_bytes": total_r, "written_bytes": total_w,
+                "fetch_factor": f_fetch, "write_factor": f_write}
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+def stats_summary(d: str, configs: str, calls: str, command: str):
+    """Per-kernel durations from rocprofv3 --kernel-trace of one bench run, per workload.
+
+    The run executes the workloads in the order given, each making `calls` attention
+    calls (warm-up + timed); dispatches of the attention kernels are assigned to the
+    workloads in that order."""
+    import csv
+    rows = sorted(csv.DictReader(open(_find_csv(d, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"]))
+    n = int(calls)
+    att = [r for r in rows if any(k in r["Kernel_Name"] for k in ATTN_KERNELS)]
+    mains = [i for i, r in enumerate(att) if "decode_split_kernel" in r["Kernel_Name"] or "prefill_kernel" in r["Kernel_Name"]]
+    print(f"command: {command}\n")
+    print("Durations from the kernel trace (rocprofv3 --kernel-trace --stats), grouped by workload.\n")
+    print("| workload | kernel | calls | average us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for ci, cfg in enumerate(configs.split(",")):
+        blk = mains[ci * n:(ci + 1) * n]
+        if not blk:
+            break
+        lo = blk[0]
+        hi = mains[(ci + 1) * n] if (ci + 1) * n < len(mains) else len(att)
+        per = {}
+        for r in att[lo:hi]:
+            per.setdefault(_short_name(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        call_total = 0.0
+        for k, v in per.items():
+            call_total += sum(v) / len(v)
+            print(f"| {cfg} | {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+        print(f"| {cfg} | whole attention call (sum of averages) | | {call_total:.1f} | | |")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-summary":
+        traffic_summary(*sys.argv[2:8])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--stats-summary":
+        stats_summary(*sys.argv[2:6])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
+        copy_calibration()
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
