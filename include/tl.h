@@ -106,7 +106,8 @@ int tl_kv_cache_write(const tl_kv_pool* pool, const float* k_new, const float* v
  * token per sequence; section 2: gather the pages the block table names, f32 dots,
  * masked softmax; section 3: sliding window).  Split-K over the context, then a merge.
  *   q             [batch][num_q_heads][head_dim] f32, the new token's queries
- *   block_tables  [batch][max_blocks] int32 page ids; entries past ceil(len/S) unused
+ *   block_tables  [batch][max_blocks] int32 page ids; entries past ceil(len/S) may
+ *                 be read (the row must hold max_blocks entries) but are never used
  *   seq_lens      [batch] int32, positions held INCLUDING the new token, whose
  *                 position is seq_lens[b]-1 (its K/V must already be written);
  *                 0 gives an all-zero output row
@@ -114,7 +115,11 @@ int tl_kv_cache_write(const tl_kv_pool* pool, const float* k_new, const float* v
  *   scale         multiplies q.k (e.g. 1/sqrt(head_dim))
  *   out           [batch][num_q_heads][head_dim] f32
  *   workspace     device scratch of at least tl_paged_attn_decode_workspace_size(...)
- *                 bytes (partial softmax states); contents need no initialisation
+ *                 bytes: partial softmax states and a work counter.  It must be
+ *                 zero-filled before its first use; every call leaves the counter
+ *                 at zero again, so it can be reused by later calls on the same
+ *                 stream without clearing.  Two calls in flight at once (on
+ *                 different streams) need separate workspaces.
  * Query head h reads kv head h / (num_q_heads / num_kv_heads).
  * Results depend only on each sequence's own inputs (no cross-sequence reductions),
  * so a sequence's output is the same bits in any batch.

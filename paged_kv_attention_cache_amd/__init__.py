@@ -168,7 +168,7 @@ def tl_paged_attn_decode(pool: KVPool, q, block_tables, seq_lens, window: int = 
         out = torch.empty_like(q)
     if workspace is None:
         nbytes = tl_paged_attn_decode_workspace_size(pool, B, Hq, max_blocks)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)  # zero before first use
     ps = pool.c_struct()
     sc = default_scale(D) if scale is None else scale
     _check(lib().tl_paged_attn_decode(ctypes.byref(ps), q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks,

@@ -80,13 +80,13 @@ __device__ __forceinline__ void load_k(KBuf<KVT, D>& t, const DecodeArgs& a, con
   const uint4* base = reinterpret_cast<const uint4*>(a.pool.k) + (((int64_t)page * H + sp.kvh) * GE::NC) * S +
                       (key & (S - 1));
 #pragma unroll
-  for (int c = 0; c < GE::NC; ++c) t.k[c] = base[(int64_t)c * S];
+  for (int c = 0; c < GE::NC; ++c) t.k[c] = stream_load(base + (int64_t)c * S);
   if constexpr (KVT == KV_FP8) {
     const int g0 = clampi(k0 + kg * 4, sp.lo & ~3, sp.hi & ~3);
     const int pg = page_of_lane(sp.tab, clampi((g0 >> sh) - sp.first_block, 0, 63));
     const int64_t idx = ((int64_t)pg * H + sp.kvh) * S + (g0 & (S - 1));
-    t.ks = *reinterpret_cast<const v4f*>(a.pool.k_scale + idx);
-    t.vs = *reinterpret_cast<const v4f*>(a.pool.v_scale + idx);
+    t.ks = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.k_scale + idx));
+    t.vs = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.v_scale + idx));
   }
 }
 
@@ -110,15 +110,16 @@ __device__ __forceinline__ void load_v(VBuf<KVT, D>& t, const DecodeArgs& a, con
       const char* r = row + i * D * GE::Tr::BYTES;
       uint32_t* dst = t.v[8 * g + i];
       if constexpr (GE::VW == 16) {
-        uint4 x = *reinterpret_cast<const uint4*>(r);
+        const uint4 x = stream_load(reinterpret_cast<const uint4*>(r));
         dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
       } else if constexpr (GE::VW == 8) {
-        uint2 x = *reinterpret_cast<const uint2*>(r);
-        dst[0] = x.x; dst[1] = x.y;
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        const u2 x = __builtin_nontemporal_load(reinterpret_cast<const u2*>(r));
+        dst[0] = x[0]; dst[1] = x[1];
       } else if constexpr (GE::VW == 4) {
-        dst[0] = *reinterpret_cast<const uint32_t*>(r);
+        dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(r));
       } else {  // fp8 with D = 64: 2 bytes
-        dst[0] = *reinterpret_cast<const uint16_t*>(r);
+        dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(r));
       }
     }
   }
@@ -221,17 +222,20 @@ __device__ __forceinline__ v4f quad_transpose(v4f x, int j) {
 }
 // One tile: issue this tile's V rows and the next tile's K chunks, then scores on the
 // current K, online softmax, and values.
-template <int KVT, int D, bool PF>
+struct NoHook { __device__ __forceinline__ void operator()() const {} };
+
+template <int KVT, int D, bool PF, typename Hook = NoHook>
 __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp, KBuf<KVT, D>& kc,
-                                            KBuf<KVT, D>& kn, VBuf<KVT, D>& vt, int k0, const float* q, v4f* o,
-                                            float& m, float& l) {
+                                            KBuf<KVT, D>& kn, VBuf<KVT, D>& vt, int k0, int k_next,
+                                            const float* q, v4f* o, float& m, float& l, Hook hook = Hook()) {
   using GE = Geo<KVT, D>;
   const int kg = (sp.lane >> 2) & 7, j = sp.lane & 3;
   if constexpr (!PF) load_k<KVT, D>(kc, a, sp, k0);
   load_v<KVT, D>(vt, a, sp, k0);
   if constexpr (PF) {
-    if (k0 + TK <= sp.k_end) load_k<KVT, D>(kn, a, sp, k0 + TK);
+    if (k_next <= sp.k_end) load_k<KVT, D>(kn, a, sp, k_next);
   }
+  hook();  // loads for later work, issued behind this tile's own
 
   // ---- scores, then lane (kg, j) register r = S[head j][key kg*4 + r]
   v4f sc = quad_transpose(qk_tile<KVT, D>(kc, q), j);
@@ -279,115 +283,367 @@ __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp
   else pv_tile<KVT, D, true>(vt, pv, o, kk_lo, kk_hi);
 }
 
-template <int KVT, int D, int G>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  using GE = Geo<KVT, D>;
-  constexpr int NT = GE::NT, NQ = GE::NQ;
-  const int lane = threadIdx.x;
-  const int slot = lane >> 5, kg = (lane >> 2) & 7, j = lane & 3;
-  const int split = blockIdx.x, b = blockIdx.z;
-  const int H = a.pool.num_kv_heads;
-  // slot -> kv head and the q heads it holds
-  int kvh, qh_base;
-  bool slot_on;
+#ifndef TL_DECODE_WAVES
+#define TL_DECODE_WAVES 4
+#endif
+constexpr int NWD = TL_DECODE_WAVES;  // waves per workgroup; they share one split
+constexpr int NTHR = 64 * NWD;
+#ifndef TL_DECODE_MIN_WAVES
+#define TL_DECODE_MIN_WAVES 2
+#endif
+// waves per SIMD the register budget is sized for (f32 tiles need twice the registers)
+template <int KVT> struct DecodeOcc { static constexpr int value = KVT == KV_F32 ? 1 : TL_DECODE_MIN_WAVES; };
+
+// ---------------------------------------------------------------- work items
+// A work item is one split of one sequence for one head group.  Items are numbered
+// densely, longest first: every sequence's whole splits, then the partial ones (a
+// sequence's first split when the window cuts into it, its last when the length is
+// not a multiple of the split size) in NBKT buckets of decreasing tile count.
+// Workgroups are persistent and take items in that order (the first two statically,
+// then from a counter in the workspace), so the launch ends on its shortest items and
+// no workgroup is spent on a split that does not exist.  Every workgroup rebuilds the
+// numbering in LDS from the lengths (prefix sums over the batch).
+constexpr int NBKT = 4;
+
+struct SeqSplits { int lo, hi, s_first, s_last, f_first, f_last, nf, part[2], np; };
+
+__device__ __forceinline__ SeqSplits seq_splits(const DecodeArgs& a, int L) {
+  SeqSplits r;
+  const int sk = a.split_keys;
+  L = min(L, a.max_blocks * a.pool.page_size);
+  r.np = 0;
+  r.part[0] = r.part[1] = 0;
+  if (L <= 0) {
+    r.lo = 0; r.hi = -1; r.s_first = 0; r.s_last = -1; r.f_first = 0; r.f_last = -1; r.nf = 0;
+    return r;
+  }
+  r.hi = L - 1;
+  r.lo = a.window > 0 ? max(0, L - a.window) : 0;
+  r.s_first = r.lo / sk;
+  r.s_last = r.hi / sk;
+  r.f_first = (r.lo + sk - 1) / sk;  // first split wholly inside [lo, hi]
+  r.f_last = (r.hi + 1) / sk - 1;    // last one
+  r.nf = max(0, r.f_last - r.f_first + 1);
+  if (r.s_first < r.f_first || r.s_first > r.f_last) r.part[r.np++] = r.s_first;
+  if (r.s_last != r.s_first && (r.s_last < r.f_first || r.s_last > r.f_last)) r.part[r.np++] = r.s_last;
+  return r;
+}
+
+// tiles of split s (its keys inside [lo, hi], from a 32-key boundary)
+__device__ __forceinline__ int split_tiles(const DecodeArgs& a, const SeqSplits& ss, int s) {
+  const int k_begin = max(s * a.split_keys, ss.lo) & ~(TK - 1);
+  const int k_end = min((s + 1) * a.split_keys - 1, ss.hi);
+  return (k_end - k_begin) / TK + 1;
+}
+
+__device__ __forceinline__ int tile_bucket(const DecodeArgs& a, int tiles) {
+  const int per = a.split_keys / TK;
+  return min(NBKT - 1, (tiles - 1) * NBKT / per);
+}
+
+// first index b in [0, n) with incl[b] > x (incl non-decreasing, incl[n-1] > x)
+__device__ __forceinline__ int lds_upper(const int* incl, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (incl[mid] > x) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// The LDS tables: per sequence its length and the inclusive prefix sums of its whole
+// splits and of its partial splits in each bucket.
+struct ItemTables {
+  int* len;
+  int* full;
+  int* bkt[NBKT];
+};
+constexpr int TABLE_INTS = 2 + NBKT;  // ints of LDS per sequence
+
+// Item number -> (sequence, head group, split).  Workgroup-uniform.
+struct Item { int b, y, split; };
+__device__ __forceinline__ Item item_of(const DecodeArgs& a, const ItemTables& t, int it, int gy) {
+  Item r;
+  const int n = a.batch;
+  int pair = it / gy;
+  r.y = it - pair * gy;
+  const int n_full = t.full[n - 1];
+  if (pair < n_full) {
+    r.b = lds_upper(t.full, n, pair);
+    const SeqSplits ss = seq_splits(a, t.len[r.b]);
+    r.split = ss.f_first + (pair - (t.full[r.b] - ss.nf));
+    return r;
+  }
+  pair -= n_full;
+  int k = NBKT - 1;
+  for (; k > 0; --k) {  // buckets of longer splits first
+    if (pair < t.bkt[k][n - 1]) break;
+    pair -= t.bkt[k][n - 1];
+  }
+  r.b = lds_upper(t.bkt[k], n, pair);
+  const SeqSplits ss = seq_splits(a, t.len[r.b]);
+  const int before = t.bkt[k][r.b] - (r.b > 0 ? t.bkt[k][r.b - 1] : 0);  // this sequence's count in k
+  int local = pair - (t.bkt[k][r.b] - before);
+  r.split = ss.part[0];
+  for (int u = 0; u < ss.np; ++u) {
+    if (tile_bucket(a, split_tiles(a, ss, ss.part[u])) != k) continue;
+    if (local-- == 0) { r.split = ss.part[u]; break; }
+  }
+  return r;
+}
+
+// Per-wave operands of an item that do not depend on its length: the block-table
+// entries of the split (one per lane; a split spans at most 64 pages) and the raw
+// queries.  They are only loaded here; the scale is applied when the item starts, so
+// loads issued for the next item are not waited on before then.
+template <int D>
+struct ItemOps {
+  int tab;
+  float q[D / 8];
+};
+
+// first q head of this lane's slot, and whether the lane's head exists
+template <int G>
+__device__ __forceinline__ void item_heads(const DecodeArgs& a, int y, int lane, int& qh_base, bool& head_on) {
+  const int slot = lane >> 5, j = lane & 3;
   if constexpr (G == 8) {
-    kvh = blockIdx.y; qh_base = kvh * 8 + slot * 4; slot_on = true;
+    qh_base = y * 8 + slot * 4;
+    head_on = true;
   } else {
-    kvh = blockIdx.y * 2 + slot; slot_on = kvh < H; qh_base = kvh * G;
-    if (!slot_on) kvh = H - 1;  // keep addresses valid; results are discarded
+    const int kvh = y * 2 + slot;
+    qh_base = kvh * G;
+    head_on = kvh < a.pool.num_kv_heads && (G >= 4 || j < G);
   }
-  const bool head_on = slot_on && (G >= 4 || j < G);
+}
 
-  const int L = min(a.seq_lens[b], a.max_blocks * a.pool.page_size);
-  if (L <= 0) return;
-  const int hi = L - 1;
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  const int s_first = lo / a.split_keys, s_last = hi / a.split_keys;
-  if (split < s_first || split > s_last) return;
-  const int k_begin = max(split * a.split_keys, lo) & ~(TK - 1);
-  const int k_end = min((split + 1) * a.split_keys - 1, hi);  // inclusive
-
-  Split sp;
-  sp.kvh = kvh; sp.lo = lo; sp.hi = hi; sp.k_end = k_end; sp.lane = lane;
-  // the split's block-table entries, one per lane (a split spans at most 64 pages)
-  sp.first_block = k_begin >> a.pool.page_shift;
-  {
-    const int last_block = k_end >> a.pool.page_shift;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-    sp.tab = clampi(table[min(sp.first_block + lane, last_block)], 0, a.pool.num_pages - 1);
-  }
-
-  // queries: register t of lane (slot, kg, j) holds Q[head j][d = 8t + kg] * scale * log2(e)
-  float q[NQ];
-  {
-    const float* qp = a.q + ((int64_t)b * a.num_q_heads + qh_base + j) * D + kg;
+template <int D, int G>
+__device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane, ItemOps<D>& op) {
+  const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
+  op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + min(first_block + lane, a.max_blocks - 1)];
+  int qh_base;
+  bool head_on;
+  item_heads<G>(a, it.y, lane, qh_base, head_on);
+  // register t of lane (slot, kg, j) holds Q[head j][d = 8t + kg], read from a valid
+  // head whatever the lane (an absent head is zeroed by its scale)
+  const int kg = (lane >> 2) & 7, j = lane & 3;
+  const int hq = min(qh_base + j, a.num_q_heads - 1);
+  const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + hq) * D + kg;
 #pragma unroll
-    for (int t = 0; t < NQ; ++t) q[t] = head_on ? qp[8 * t] * a.qscale : 0.0f;
-  }
+  for (int t = 0; t < D / 8; ++t) op.q[t] = qp[8 * t];
+}
 
-  v4f o[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) o[i] = v4f{0, 0, 0, 0};
-  float m = -INFINITY, l = 0.0f;
-
-  // K of the next tile is prefetched into a second buffer where registers allow it
-  // (fp8); otherwise each tile loads its own K and relies on more waves per SIMD.
+// Persistent workgroups of NWD waves.  For each claimed item, wave w takes the
+// split's tiles w, w + NWD, ... with its own softmax state; the NWD states are then
+// combined through LDS in wave order, so the result depends on the split alone, not
+// on which workgroup ran it or when.  Item numbers are claimed two items ahead, and
+// each wave issues the next item's table entries and queries together with the loads
+// of its last tile of the current item, so a new item starts without waiting.
+template <int KVT, int D, int G>
+__global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kernel(DecodeArgs a) {
+  using GE = Geo<KVT, D>;
+  constexpr int NT = GE::NT;
   constexpr bool PF = DecodePrefetch<KVT, D>::value;
-  KBuf<KVT, D> kA, kB;
-  VBuf<KVT, D> vt;
-  if constexpr (PF) load_k<KVT, D>(kA, a, sp, k_begin);
-  for (int k0 = k_begin;;) {
-    decode_tile<KVT, D, PF>(a, sp, kA, kB, vt, k0, q, o, m, l);
-    k0 += TK;
-    if (k0 > k_end) break;
-    decode_tile<KVT, D, PF>(a, sp, kB, kA, vt, k0, q, o, m, l);
-    k0 += TK;
-    if (k0 > k_end) break;
-  }
+  constexpr int STEP = NWD * TK;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int slot = lane >> 5, kg = (lane >> 2) & 7, j = lane & 3;
+  const int H = a.pool.num_kv_heads;
+  const int gy = (G == 8) ? H : (H + 1) / 2;
 
-  // ---- finish: l per head summed over the slot's key groups
-  l = wave_xor_sum(l, 4);
-  l = wave_xor_sum(l, 8);
-  l = wave_xor_sum(l, 16);
-  const float lr[4] = {quad_bcast<0>(l), quad_bcast<1>(l), quad_bcast<2>(l), quad_bcast<3>(l)};
-  const int d0 = (lane & 31) * NT;
-  const bool single = (s_first == s_last);
+  extern __shared__ int dyn[];  // [TABLE_INTS][batch]
+  ItemTables tabs;
+  tabs.len = dyn;
+  tabs.full = dyn + a.batch;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (!slot_on || (G < 4 && r >= G)) continue;
-    const int hq = qh_base + r;
-    float vals[NT];
-    if (single) {
-      const float inv = lr[r] > 0.0f ? 1.0f / lr[r] : 0.0f;
+  for (int k = 0; k < NBKT; ++k) tabs.bkt[k] = dyn + (2 + k) * a.batch;
+  __shared__ int c_carry[1 + NBKT], c_wsum[NWD][1 + NBKT], s_claim[1];
+  __shared__ float c_acc[NWD][NT * 4][64];    // [wave][value i*4 + r][lane]
+  __shared__ float c_m[NWD][8], c_l[NWD][8];  // [wave][slot*4 + head]
+
+  // ---- numbering tables (inclusive block scans over the batch, NTHR at a time)
+  if (tid <= NBKT) c_carry[tid] = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < a.batch; c0 += NTHR) {
+    const int b = c0 + tid;
+    int cnt[1 + NBKT];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) vals[i] = lr[r] > 0.0f ? o[i][r] * inv : 0.0f;
-      float* dst = a.out + ((int64_t)b * a.num_q_heads + hq) * D + d0;
-#pragma unroll
-      for (int i = 0; i < NT; i += 2) *reinterpret_cast<float2*>(dst + i) = make_float2(vals[i], vals[i + 1]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NT; ++i) vals[i] = o[i][r];
-      float* dst = a.ws_acc + (((int64_t)b * a.num_q_heads + hq) * a.n_split + split) * D + d0;
-#pragma unroll
-      for (int i = 0; i < NT; i += 2) *reinterpret_cast<float2*>(dst + i) = make_float2(vals[i], vals[i + 1]);
+    for (int k = 0; k <= NBKT; ++k) cnt[k] = 0;
+    if (b < a.batch) {
+      const int L = a.seq_lens[b];
+      const SeqSplits ss = seq_splits(a, L);
+      cnt[0] = ss.nf;
+      for (int u = 0; u < ss.np; ++u) cnt[1 + tile_bucket(a, split_tiles(a, ss, ss.part[u]))] += 1;
+      tabs.len[b] = L;
     }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+      for (int k = 0; k <= NBKT; ++k) {
+        const int x = __shfl_up(cnt[k], d, 64);
+        if (lane >= d) cnt[k] += x;
+      }
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int k = 0; k <= NBKT; ++k) c_wsum[w][k] = cnt[k];
+    }
+    __syncthreads();
+    int base[1 + NBKT];
+#pragma unroll
+    for (int k = 0; k <= NBKT; ++k) {
+      base[k] = c_carry[k];
+      for (int u = 0; u < w; ++u) base[k] += c_wsum[u][k];
+    }
+    if (b < a.batch) {
+      tabs.full[b] = base[0] + cnt[0];
+#pragma unroll
+      for (int k = 0; k < NBKT; ++k) tabs.bkt[k][b] = base[1 + k] + cnt[1 + k];
+    }
+    __syncthreads();
+    if (tid == NTHR - 1) {
+#pragma unroll
+      for (int k = 0; k <= NBKT; ++k) c_carry[k] = base[k] + cnt[k];
+    }
+    __syncthreads();
   }
-  if (!single && kg == 0 && head_on) {
-    const int hq = qh_base + j;
-    float* dst = a.ws_ml + (((int64_t)b * a.num_q_heads + hq) * a.n_split + split) * 2;
-    *reinterpret_cast<float2*>(dst) = make_float2(m, l);
+  int n_pairs = tabs.full[a.batch - 1];
+#pragma unroll
+  for (int k = 0; k < NBKT; ++k) n_pairs += tabs.bkt[k][a.batch - 1];
+  const int n_items = n_pairs * gy;
+  // the first two items of each workgroup are fixed; later ones come from the counter
+  const int n_wg = gridDim.x;
+  int cur = blockIdx.x, nxt = blockIdx.x + n_wg;
+  if (cur >= n_items) return;  // workgroup-uniform
+  Item it = item_of(a, tabs, cur, gy);
+  ItemOps<D> op, nop;
+  item_ops<D, G>(a, it, lane, op);
+  Item nit = it;
+  if (nxt < n_items) nit = item_of(a, tabs, nxt, gy);
+
+  for (;;) {
+    __syncthreads();  // the previous item's combine is done everywhere
+    int claimed = 0;
+    if (tid == 0) claimed = 2 * n_wg + atomicAdd(a.ws_ctrl, 1);  // the item after nxt
+
+    // ---- this item
+    int kvh, qh_base;
+    bool slot_on;
+    if constexpr (G == 8) {
+      kvh = it.y; qh_base = kvh * 8 + slot * 4; slot_on = true;
+    } else {
+      kvh = it.y * 2 + slot; slot_on = kvh < H; qh_base = kvh * G;
+      if (!slot_on) kvh = H - 1;  // keep addresses valid; results are discarded
+    }
+    float q[D / 8];
+    {
+      int qb;
+      bool head_on;
+      item_heads<G>(a, it.y, lane, qb, head_on);
+      const float qs = head_on ? a.qscale : 0.0f;  // scores come out in log2 units
+#pragma unroll
+      for (int t = 0; t < D / 8; ++t) q[t] = op.q[t] * qs;
+    }
+    const SeqSplits ss = seq_splits(a, tabs.len[it.b]);
+    const int k_begin = max(it.split * a.split_keys, ss.lo) & ~(TK - 1);
+    const int k_end = min((it.split + 1) * a.split_keys - 1, ss.hi);  // inclusive
+    Split sp;
+    sp.kvh = kvh; sp.lo = ss.lo; sp.hi = ss.hi; sp.k_end = k_end; sp.lane = lane;
+    sp.first_block = (it.split * a.split_keys) >> a.pool.page_shift;
+    sp.tab = clampi(op.tab, 0, a.pool.num_pages - 1);
+
+    v4f o[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) o[i] = v4f{0, 0, 0, 0};
+    float m = -INFINITY, l = 0.0f;
+
+    // K of the wave's next tile is prefetched into the other buffer where registers
+    // allow it (fp8, D = 64); otherwise each tile loads its own K.  The wave's last
+    // tile is peeled so the next item's operands load with it.
+    const bool has_next = nxt < n_items;
+    auto next_ops = [&]() { if (has_next) item_ops<D, G>(a, nit, lane, nop); };
+    KBuf<KVT, D> kA, kB;
+    VBuf<KVT, D> vt;
+    int k0 = k_begin + w * TK;
+    int par = 0;
+    if (k0 <= k_end) {
+      if constexpr (PF) load_k<KVT, D>(kA, a, sp, k0);
+      while (k0 + STEP <= k_end) {
+        decode_tile<KVT, D, PF>(a, sp, kA, kB, vt, k0, k0 + STEP, q, o, m, l);
+        k0 += STEP;
+        if (k0 + STEP > k_end) { par = 1; break; }
+        decode_tile<KVT, D, PF>(a, sp, kB, kA, vt, k0, k0 + STEP, q, o, m, l);
+        k0 += STEP;
+      }
+      if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vt, k0, k0 + STEP, q, o, m, l, next_ops);
+      else decode_tile<KVT, D, PF>(a, sp, kB, kA, vt, k0, k0 + STEP, q, o, m, l, next_ops);
+    } else {
+      next_ops();
+    }
+
+    // ---- l per head summed over the slot's key groups; the wave's state to LDS
+    l = wave_xor_sum(l, 4);
+    l = wave_xor_sum(l, 8);
+    l = wave_xor_sum(l, 16);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c_acc[w][i * 4 + r][lane] = o[i][r];
+    if (kg == 0) { c_m[w][slot * 4 + j] = m; c_l[w][slot * 4 + j] = l; }
+    if (tid == 0) s_claim[0] = claimed;
+    __syncthreads();
+
+    // ---- combine in wave order: value v = i*4 + r of this lane is head slot*4 + r,
+    // d = (lane % 32) * NT + i; wave w finishes the values v with v % NWD == w.
+    const bool single = (ss.s_first == ss.s_last);
+    const int d_base = (lane & 31) * NT;
+#pragma unroll
+    for (int v = 0; v < NT * 4; ++v) {
+      if (v % NWD != w) continue;
+      const int i = v >> 2, r = v & 3;
+      if (!slot_on || (G < 4 && r >= G)) continue;
+      const int h = slot * 4 + r;
+      float ms = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NWD; ++u) ms = fmaxf(ms, c_m[u][h]);
+      const float mu = (ms == -INFINITY) ? 0.0f : ms;
+      float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < NWD; ++u) {
+        const float wt = fast_exp2(c_m[u][h] - mu);
+        lsum += wt * c_l[u][h];
+        acc += wt * c_acc[u][v][lane];
+      }
+      const int hq = qh_base + r, d = d_base + i;
+      if (single) {
+        a.out[((int64_t)it.b * a.num_q_heads + hq) * D + d] = lsum > 0.0f ? acc * (1.0f / lsum) : 0.0f;
+      } else {
+        a.ws_acc[(((int64_t)it.b * a.num_q_heads + hq) * a.n_split + it.split) * D + d] = acc;
+        if (i == 0 && (lane & 31) == 0) {
+          float* dst = a.ws_ml + (((int64_t)it.b * a.num_q_heads + hq) * a.n_split + it.split) * 2;
+          *reinterpret_cast<float2*>(dst) = make_float2(ms, lsum);
+        }
+      }
+    }
+    if (!has_next) break;  // workgroup-uniform
+    const int nn = s_claim[0];
+    it = nit;
+    op = nop;
+    nxt = nn;
+    if (nxt < n_items) nit = item_of(a, tabs, nxt, gy);
   }
 }
 
 // Combine the splits of each (sequence, q head): m* = max m_s,
 // o = sum 2^(m_s - m*) acc_s / sum 2^(m_s - m*) l_s (log2 units).  Sequences with one
-// split were finished by the split kernel; empty sequences get zeros.
+// split were finished by the split kernel; empty sequences get zeros.  Lane s holds
+// split s's (m, l) (64 splits per pass), so the max and the sum over splits are wave
+// reductions; the accumulators are read eight splits per batch of loads.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.num_q_heads;
   const int lane = threadIdx.x;
   constexpr int PER = D / 64;
+  if (bh == 0 && lane == 0) a.ws_ctrl[0] = 0;  // item counter, for the next call
   float* dst = a.out + (int64_t)bh * D + lane * PER;
   const int L = min(a.seq_lens[b], a.max_blocks * a.pool.page_size);
   if (L <= 0) {
@@ -399,36 +655,85 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
   const int s0 = lo / a.split_keys, s1 = hi / a.split_keys;
   if (s0 == s1) return;
-  const float* ml = a.ws_ml + (int64_t)bh * a.n_split * 2;
-  const float* acc = a.ws_acc + (int64_t)bh * a.n_split * D + lane * PER;
+  const int ns = s1 - s0 + 1;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (int64_t)bh * a.n_split + s0;
+  const float* acc = a.ws_acc + ((int64_t)bh * a.n_split + s0) * D + lane * PER;
   float mstar = -INFINITY;
-  for (int s = s0; s <= s1; ++s) mstar = fmaxf(mstar, ml[2 * s]);
+  for (int c = lane; c < ns; c += 64) mstar = fmaxf(mstar, ml[c].x);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mstar = wave_xor_max(mstar, m);
   if (mstar == -INFINITY) mstar = 0.0f;
   float o[PER] = {};
   float l = 0.0f;
-  for (int s = s0; s <= s1; ++s) {
-    const float w = fast_exp2(ml[2 * s] - mstar);
-    l += w * ml[2 * s + 1];
+  for (int c = 0; c < ns; c += 64) {
+    float w = 0.0f;
+    if (c + lane < ns) {
+      const float2 x = ml[c + lane];
+      w = fast_exp2(x.x - mstar);
+      l += w * x.y;
+    }
+    const int n = min(64, ns - c);
+    for (int u0 = 0; u0 < n; u0 += 8) {
+      float av[8][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] += w * acc[(int64_t)s * D + i];
+      for (int u = 0; u < 8; ++u) {
+        const int s = c + min(u0 + u, n - 1);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) av[u][i] = acc[(int64_t)s * D + i];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = (u0 + u < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u0 + u)) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += wu * av[u][i];
+      }
+    }
   }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) l = wave_xor_sum(l, m);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) dst[i] = l > 0.0f ? o[i] * inv : 0.0f;
 }
 
+// Resident workgroups of one kernel instantiation at a given dynamic LDS size.
+template <typename K>
+int resident_workgroups(K kernel, size_t dyn_lds) {
+  static int cached = 0;
+  static size_t cached_lds = 0;
+  if (cached == 0 || cached_lds != dyn_lds) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NTHR, dyn_lds) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached = per_cu * cus;
+    cached_lds = dyn_lds;
+  }
+  return cached;
+}
+
+template <int KVT, int D, int G>
+hipError_t decode_launch_split(const DecodeArgs& a, hipStream_t s) {
+  const int H = a.pool.num_kv_heads;
+  const int64_t gy = (G == 8) ? H : (H + 1) / 2;
+  const size_t dyn = (size_t)TABLE_INTS * a.batch * sizeof(int);
+  const int64_t upper = (int64_t)a.batch * a.n_split * gy;
+  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups(decode_split_kernel<KVT, D, G>, dyn));
+  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G>), dim3((unsigned)wgs), dim3(NTHR), dyn, s, a);
+  return hipGetLastError();
+}
+
 template <int KVT, int D>
 hipError_t decode_dispatch_g(const DecodeArgs& a, hipStream_t s) {
-  const int H = a.pool.num_kv_heads;
-  const unsigned gy = (a.group == 8) ? H : (H + 1) / 2;
-  const dim3 grid(a.n_split, gy, a.batch);
+  hipError_t e;
   switch (a.group) {
-    case 8: hipLaunchKernelGGL((decode_split_kernel<KVT, D, 8>), grid, dim3(64), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<KVT, D, 4>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<KVT, D, 2>), grid, dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<KVT, D, 1>), grid, dim3(64), 0, s, a); break;
+    case 8: e = decode_launch_split<KVT, D, 8>(a, s); break;
+    case 4: e = decode_launch_split<KVT, D, 4>(a, s); break;
+    case 2: e = decode_launch_split<KVT, D, 2>(a, s); break;
+    default: e = decode_launch_split<KVT, D, 1>(a, s); break;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.num_q_heads), dim3(64), 0, s, a);
   return hipGetLastError();
@@ -444,17 +749,38 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
 
 int decode_split_keys(int kv_dtype, int group, int page_size) {
   (void)group;
-  const int want = kv_dtype == KV_FP8 ? 1024 : 512;
+#ifndef TL_DECODE_SPLIT_FP8
+#define TL_DECODE_SPLIT_FP8 1024
+#endif
+#ifndef TL_DECODE_SPLIT_OTHER
+#define TL_DECODE_SPLIT_OTHER 512
+#endif
+  const int want = kv_dtype == KV_FP8 ? TL_DECODE_SPLIT_FP8 : TL_DECODE_SPLIT_OTHER;
   return want < 64 * page_size ? want : 64 * page_size;  // a split spans at most 64 pages
 }
 
+// Batches larger than DECODE_BATCH_CHUNK run as consecutive launches over slices of
+// the batch (the per-workgroup item tables hold 12 bytes of LDS per sequence).
+// Sequences are independent, so a slice computes exactly what the whole batch would.
+constexpr int DECODE_BATCH_CHUNK = 2048;
+
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s) {
-  if (a.batch == 0) return hipSuccess;
-  switch (kv_dtype) {
-    case KV_F32: return decode_dispatch<KV_F32>(a, s);
-    case KV_BF16: return decode_dispatch<KV_BF16>(a, s);
-    default: return decode_dispatch<KV_FP8>(a, s);
+  for (int b0 = 0; b0 < a.batch; b0 += DECODE_BATCH_CHUNK) {
+    DecodeArgs c = a;
+    c.batch = std::min(DECODE_BATCH_CHUNK, a.batch - b0);
+    c.q = a.q + (int64_t)b0 * a.num_q_heads * a.pool.head_dim;
+    c.out = a.out + (int64_t)b0 * a.num_q_heads * a.pool.head_dim;
+    c.block_tables = a.block_tables + (int64_t)b0 * a.max_blocks;
+    c.seq_lens = a.seq_lens + b0;
+    hipError_t e;
+    switch (kv_dtype) {
+      case KV_F32: e = decode_dispatch<KV_F32>(c, s); break;
+      case KV_BF16: e = decode_dispatch<KV_BF16>(c, s); break;
+      default: e = decode_dispatch<KV_FP8>(c, s); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace tl

@@ -59,6 +59,15 @@ __device__ __forceinline__ void widen_chunk(const uint4& c, float* o) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load marked nontemporal: data read once (the KV pages of a decode step)
+// stream through the caches without displacing other lines, which also sustains a
+// higher HBM read rate than plain loads.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4 x = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // broadcast lane (lane & ~3) | R of each quad to the whole quad (DPP quad_perm)
 template <int R>
 __device__ __forceinline__ float quad_bcast(float v) {
@@ -108,6 +117,7 @@ struct DecodeArgs {
   float* out;
   float* ws_acc;   // [batch][num_q_heads][n_split][head_dim]
   float* ws_ml;    // [batch][num_q_heads][n_split][2]
+  int* ws_ctrl;    // [4]: the item counter (zero between calls)
   int num_q_heads, group, max_blocks, batch, window, split_keys, n_split;
   float qscale;    // scale * log2(e): scores come out in log2 units
 };

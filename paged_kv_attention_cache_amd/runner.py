@@ -50,7 +50,7 @@ class DecodeStep:
         self.seq_lens = _t(wl.seq_lens, device)
         self.out = torch.empty_like(self.q)
         nb = tl_paged_attn_decode_workspace_size(pool, wl.batch, wl.num_q_heads, wl.max_blocks)
-        self.workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+        self.workspace = torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)
 
     def write(self, stream=None):
         tl_kv_cache_write(self.pool, self.k_new, self.v_new, self.slots, stream=stream)
