@@ -60,8 +60,12 @@ __device__ __forceinline__ int page_uniform(int tab, int local) { return __built
 #ifndef TL_DECODE_PREFETCH_BF16
 #define TL_DECODE_PREFETCH_BF16 0
 #endif
-template <int KVT, int D> struct DecodePrefetch {
-  static constexpr bool value = (KVT == KV_FP8) || (KVT == KV_BF16 && TL_DECODE_PREFETCH_BF16) || D == 64;
+// How far ahead a wave loads: 0 = each tile loads its own K and V; 1 = the next
+// tile's K is loaded with this tile's V; 2 = the next tile's K and V are loaded while
+// this tile computes.  Chosen by what fits in the register budget (fp8 tiles are
+// small; bf16 and f32 tiles at D = 128 rely on more waves per SIMD instead).
+template <int KVT, int D, int G> struct DecodePrefetch {
+  static constexpr int value = (KVT == KV_FP8 && D == 128 && G == 8) ? 2 : (D == 64 ? 1 : 0);
 };
 
 struct Split {
@@ -224,16 +228,24 @@ __device__ __forceinline__ v4f quad_transpose(v4f x, int j) {
 // current K, online softmax, and values.
 struct NoHook { __device__ __forceinline__ void operator()() const {} };
 
-template <int KVT, int D, bool PF, typename Hook = NoHook>
+template <int KVT, int D, int PF, typename Hook = NoHook>
 __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp, KBuf<KVT, D>& kc,
-                                            KBuf<KVT, D>& kn, VBuf<KVT, D>& vt, int k0, int k_next,
-                                            const float* q, v4f* o, float& m, float& l, Hook hook = Hook()) {
+                                            KBuf<KVT, D>& kn, VBuf<KVT, D>& vt, VBuf<KVT, D>& vn, int k0,
+                                            int k_next, const float* q, v4f* o, float& m, float& l,
+                                            Hook hook = Hook()) {
   using GE = Geo<KVT, D>;
   const int kg = (sp.lane >> 2) & 7, j = sp.lane & 3;
-  if constexpr (!PF) load_k<KVT, D>(kc, a, sp, k0);
-  load_v<KVT, D>(vt, a, sp, k0);
-  if constexpr (PF) {
+  if constexpr (PF == 0) {
+    load_k<KVT, D>(kc, a, sp, k0);
+    load_v<KVT, D>(vt, a, sp, k0);
+  } else if constexpr (PF == 1) {
+    load_v<KVT, D>(vt, a, sp, k0);
     if (k_next <= sp.k_end) load_k<KVT, D>(kn, a, sp, k_next);
+  } else {
+    if (k_next <= sp.k_end) {
+      load_k<KVT, D>(kn, a, sp, k_next);
+      load_v<KVT, D>(vn, a, sp, k_next);
+    }
   }
   hook();  // loads for later work, issued behind this tile's own
 
@@ -442,7 +454,7 @@ template <int KVT, int D, int G>
 __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kernel(DecodeArgs a) {
   using GE = Geo<KVT, D>;
   constexpr int NT = GE::NT;
-  constexpr bool PF = DecodePrefetch<KVT, D>::value;
+  constexpr int PF = DecodePrefetch<KVT, D, G>::value;
   constexpr int STEP = NWD * TK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int slot = lane >> 5, kg = (lane >> 2) & 7, j = lane & 3;
@@ -561,20 +573,22 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
     const bool has_next = nxt < n_items;
     auto next_ops = [&]() { if (has_next) item_ops<D, G>(a, nit, lane, nop); };
     KBuf<KVT, D> kA, kB;
-    VBuf<KVT, D> vt;
+    VBuf<KVT, D> vA, vB_;
+    VBuf<KVT, D>& vB = (PF >= 2) ? vB_ : vA;  // one V buffer unless V is prefetched
     int k0 = k_begin + w * TK;
     int par = 0;
     if (k0 <= k_end) {
-      if constexpr (PF) load_k<KVT, D>(kA, a, sp, k0);
+      if constexpr (PF >= 1) load_k<KVT, D>(kA, a, sp, k0);
+      if constexpr (PF >= 2) load_v<KVT, D>(vA, a, sp, k0);
       while (k0 + STEP <= k_end) {
-        decode_tile<KVT, D, PF>(a, sp, kA, kB, vt, k0, k0 + STEP, q, o, m, l);
+        decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l);
         k0 += STEP;
         if (k0 + STEP > k_end) { par = 1; break; }
-        decode_tile<KVT, D, PF>(a, sp, kB, kA, vt, k0, k0 + STEP, q, o, m, l);
+        decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l);
         k0 += STEP;
       }
-      if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vt, k0, k0 + STEP, q, o, m, l, next_ops);
-      else decode_tile<KVT, D, PF>(a, sp, kB, kA, vt, k0, k0 + STEP, q, o, m, l, next_ops);
+      if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, next_ops);
+      else decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l, next_ops);
     } else {
       next_ops();
     }
@@ -705,6 +719,9 @@ int resident_workgroups(K kernel, size_t dyn_lds) {
     int per_cu = 0, dev = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NTHR, dyn_lds) != hipSuccess || per_cu <= 0)
       per_cu = 1;
+#ifdef TL_DECODE_WG_PER_CU
+    per_cu = std::min(per_cu, TL_DECODE_WG_PER_CU);
+#endif
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
