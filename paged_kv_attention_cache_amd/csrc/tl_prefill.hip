@@ -132,15 +132,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  // XCD-aware work order: launch ids round-robin over 8 XCDs; give each XCD a
-  // contiguous range of (b, h, tile) so a sequence's K/V stays in one L2.
-  const int nx = gridDim.x, ny = gridDim.y;
-  const int total = nx * ny * gridDim.z;
+  // Work order: query tiles latest-first across all rows and heads (rows are
+  // right-aligned, so a later tile holds later positions and sees more keys).  The
+  // dispatcher hands out launch ids in order, round-robin over the XCDs, so the heavy
+  // tiles of every row start first and spread over the whole chip; the light ones
+  // (and the pad-only tiles, which return at once) fill the end.
+  const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
   const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-  const int work = (total % 8 == 0) ? (lin % 8) * (total / 8) + lin / 8 : lin;
-  const int tile = nx - 1 - (work % nx);  // later (heavier) query tiles first
-  const int h = (work / nx) % ny;
-  const int b = work / (nx * ny);
+  const int tile = nx - 1 - lin / (ny * nz);
+  const int h = lin % ny;
+  const int b = (lin / ny) % nz;
 
   const int T = a.tokens_per_row;
   const int tok = tile * TPG + w * TPW + col / G;
