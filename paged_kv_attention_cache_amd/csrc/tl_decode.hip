@@ -65,7 +65,7 @@ __device__ __forceinline__ int page_uniform(int tab, int local) { return __built
 // this tile computes.  Chosen by what fits in the register budget (fp8 tiles are
 // small; bf16 and f32 tiles at D = 128 rely on more waves per SIMD instead).
 template <int KVT, int D, int G> struct DecodePrefetch {
-  static constexpr int value = (KVT == KV_FP8 && D == 128 && G == 8) ? 2 : (D == 64 ? 1 : 0);
+  static constexpr int value = (KVT == KV_FP8 && D == 128 && G == 8) ? 1 : (D == 64 ? 1 : 0);
 };
 
 struct Split {
@@ -295,6 +295,246 @@ __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp
   else pv_tile<KVT, D, true>(vt, pv, o, kk_lo, kk_hi);
 }
 
+
+// ------------------------------------------------ fp8, D = 128, G = 8: exact bf16 split
+// For the fp8 pool with 8 query heads per KV head, both dots run on
+// v_mfma_f32_16x16x32_bf16 without changing the arithmetic: every fp8 K and V value
+// is exactly a bf16, and each f32 operand on the other side (the scaled query, the
+// scaled probability) is split exactly into three bf16 terms, hi + mid + lo (each the
+// truncation of what remains, 8 significant bits at a time).  The products of bf16
+// terms are exact in f32 and the matrix core sums them in f32, so a dot is still f32
+// operands, f32 products and f32 sums, only summed in a different order.
+//
+// Per wave and 32-key tile of one KV head (lane l, c = l % 16, g = l / 16):
+//   scores  S^T[key, col] = sum_d K[key, d] Q3[col, d]: two 16-key halves x two
+//           column tiles (columns: hi and mid of heads 0-7, then lo of heads 0-7 and
+//           8 zero columns) x four 32-wide d steps = 16 MFMAs.  Lane l then holds,
+//           for head c (c < 8), keys 16*h + 4g + r of the tile (h = half, r = 0..3).
+//   values  O3[row, d] += sum_key P3[row, key] V[key, d]: rows are hi and mid of
+//           heads 0-7 (tile 0) and lo (tile 1); d = 8c + n for d tile n = 0..7; the
+//           key order of the sum is that of the score lanes (key 16*(e/4) + 4g + e%4
+//           for k = 8g + e), so P stays in the lane that computed it: 16 MFMAs.
+// Per lane per tile: 8 K loads and 8 V loads of 8 bytes, no value loaded twice.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct XBuf {
+  u32x2 k[2][4];  // [half][d step]: 8 fp8 of key 16*half + c at d 32s + 8g .. +7
+  u32x2 v[8];     // [e]: 8 fp8 of key 16*(e/4) + 4g + e%4 at d 8c .. 8c+7
+  v4f ks[2], vs[2];  // [half]: scales of keys 16*half + 4g .. +3
+};
+
+__device__ __forceinline__ uint32_t bf16_pair_of(float a, float b) {
+  // a, b are exact bf16 values (low 16 bits zero): pack them as (a, b)
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+__device__ __forceinline__ float trunc_bf16(float x) { return __uint_as_float(__float_as_uint(x) & 0xFFFF0000u); }
+// x = hi + mid + lo exactly, each a bf16 value
+__device__ __forceinline__ void split3(float x, float& hi, float& mid, float& lo) {
+  hi = trunc_bf16(x);
+  const float r1 = x - hi;
+  mid = trunc_bf16(r1);
+  lo = trunc_bf16(r1 - mid);
+}
+// lane i of each 16-lane row receives lane i ^ 8 (DPP row rotate by 8)
+__device__ __forceinline__ uint32_t ror8(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); }
+__device__ __forceinline__ float ror8f(float v) { return __uint_as_float(ror8(__float_as_uint(v))); }
+
+// two fp8 codes (bytes 2W, 2W+1 of x) -> packed bf16 pair, exact
+template <bool W>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, W);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Parts of a tile's operands, loaded separately so each can be refilled for the next
+// tile as soon as this tile has consumed it.
+struct XHalf { int64_t ph; int hk0; };
+__device__ __forceinline__ XHalf xhalf(const DecodeArgs& a, const Split& sp, int k0, int h) {
+  // a 16-key half never straddles a page (pages hold >= 16 keys here)
+  XHalf r;
+  r.hk0 = clampi(k0 + 16 * h, sp.lo & ~15, sp.hi & ~15);
+  const int page = page_uniform(sp.tab, clampi((r.hk0 >> a.pool.page_shift) - sp.first_block, 0, 63));
+  r.ph = (int64_t)page * a.pool.num_kv_heads + sp.kvh;
+  return r;
+}
+__device__ __forceinline__ void xload_k(XBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  constexpr int NC = 128 / 16;
+  const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const XHalf x = xhalf(a, sp, k0, h);
+    // key clamped into [lo, hi]; chunk 2s + g/2, byte half g%2
+    const int key = clampi(x.hk0 + c, sp.lo, sp.hi);
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(a.pool.k) +
+                              ((x.ph * NC + (g >> 1)) * S + (key & (S - 1))) * 16 + 8 * (g & 1);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      t.k[h][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kb + (int64_t)2 * st * S * 16));
+  }
+}
+__device__ __forceinline__ void xload_scales(XBuf& t, const DecodeArgs& a, const Split& sp, int k0, bool kside) {
+  const int S = a.pool.page_size, g = sp.lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const XHalf x = xhalf(a, sp, k0, h);
+    const int g0 = clampi(x.hk0 + 4 * g, sp.lo & ~3, sp.hi & ~3);
+    const int64_t si = x.ph * S + (g0 & (S - 1));
+    if (kside) t.ks[h] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.k_scale + si));
+    else t.vs[h] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.v_scale + si));
+  }
+}
+__device__ __forceinline__ void xload_v(XBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  constexpr int D = 128;
+  const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const XHalf x = xhalf(a, sp, k0, h);
+    // rows of keys hk0 + 4g + r, clamped into [lo, hi]; bytes 8c .. 8c+7
+    const int rlo = sp.lo - x.hk0, rhi = sp.hi - x.hk0;
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(a.pool.v) + (x.ph * S + (x.hk0 & (S - 1))) * D + 8 * c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = min(max(4 * g + r, rlo), rhi);
+      t.v[4 * h + r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + (int64_t)row * D));
+    }
+  }
+}
+__device__ __forceinline__ void xload(XBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  xload_k(t, a, sp, k0);
+  xload_scales(t, a, sp, k0, true);
+  xload_scales(t, a, sp, k0, false);
+  xload_v(t, a, sp, k0);
+}
+
+// One 32-key tile on the operands in t; each part of t is reloaded with the next
+// tile's as soon as it has been used.  qs: this wave's Q3 operands in LDS
+// ([col tile][d step][lane]); o: [row tile][d tile].  The running max m only moves
+// when a tile's max exceeds it by more than 8 (log2 units, a factor 2^8), so the
+// accumulators are rarely rescaled; probabilities then stay below 2^8.
+template <typename Hook = NoHook>
+__device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf& t, int k0, int k_next,
+                                      const bf16x8* qs, v4f (&o)[2][8], float& m, float& l, Hook hook = Hook()) {
+  const int c = sp.lane & 15, g = sp.lane >> 4;
+  const bool more = k_next <= sp.k_end;
+  // ---- scores
+  v4f sc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v4f t0 = v4f{0, 0, 0, 0}, t1 = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t w[4];
+      w[0] = fp8x2_to_bf16x2<false>(t.k[h][st][0]);
+      w[1] = fp8x2_to_bf16x2<true>(t.k[h][st][0]);
+      w[2] = fp8x2_to_bf16x2<false>(t.k[h][st][1]);
+      w[3] = fp8x2_to_bf16x2<true>(t.k[h][st][1]);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+      t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qs[(0 * 4 + st) * 64 + sp.lane], t0, 0, 0, 0);
+      t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qs[(1 * 4 + st) * 64 + sp.lane], t1, 0, 0, 0);
+    }
+    // head c: hi (column c) + mid (column c + 8) + lo (column c of tile 1)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[h][r] = (t0[r] + ror8f(t0[r])) + t1[r];
+  }
+  if (more) xload_k(t, a, sp, k_next);
+  // ---- mask, online softmax for head c over the wave's 32 keys
+  float s8[8], tmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int h = e >> 2, r = e & 3;
+    const int key = k0 + 16 * h + 4 * g + r;
+    const bool valid = key >= sp.lo && key <= sp.k_end;
+    s8[e] = valid ? sc[h][r] * t.ks[h][r] : -INFINITY;
+    tmax = fmaxf(tmax, s8[e]);
+  }
+  if (more) xload_scales(t, a, sp, k_next, true);
+  tmax = wave_xor_max(tmax, 16);
+  tmax = wave_xor_max(tmax, 32);
+  // lazy max: keep m unless this tile exceeds it by more than 8 (or m is unset)
+  const float m_new = (m == -INFINITY || tmax > m + 8.0f) ? tmax : m;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = (m == -INFINITY) ? 1.0f : fast_exp2(m - m_use);  // o and l are 0 while m is unset
+  float psum = 0.0f;
+  float ph[8], pm[8], pl[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = fast_exp2(s8[e] - m_use);
+    psum += p;
+    const float pv = (s8[e] == -INFINITY) ? 0.0f : p * t.vs[e >> 2][e & 3];
+    split3(pv, ph[e], pm[e], pl[e]);
+  }
+  if (more) xload_scales(t, a, sp, k_next, false);
+  l = l * alpha + psum;
+  m = m_new;
+  // ---- A operands of the value product: rows hi / mid (tile 0) and lo (tile 1)
+  uint32_t a0[4], a1[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const uint32_t hi2 = bf16_pair_of(ph[2 * qd], ph[2 * qd + 1]);
+    const uint32_t mid2 = ror8(bf16_pair_of(pm[2 * qd], pm[2 * qd + 1]));
+    const uint32_t lo2 = bf16_pair_of(pl[2 * qd], pl[2 * qd + 1]);
+    a0[qd] = c < 8 ? hi2 : mid2;
+    a1[qd] = c < 8 ? lo2 : 0u;
+  }
+  const bf16x8 pa0 = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a0[2], a0[3]});
+  const bf16x8 pa1 = __builtin_bit_cast(bf16x8, u32x4{a1[0], a1[1], a1[2], a1[3]});
+  // ---- rescale: accumulator row 4g + r belongs to head 4(g % 2) + r
+  if (__any(c < 8 && alpha != 1.0f)) {
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * (g & 1) + r, 64);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { o[0][n][r] *= ar[r]; o[1][n][r] *= ar[r]; }
+  }
+  // ---- values: B operand of d tile n = V[key(8g + e)][8c + n] for e = 0..7
+#pragma unroll
+  for (int np = 0; np < 4; ++np) {  // d tiles 2np, 2np + 1 share one byte gather
+    const int word = np >> 1, b0 = (np & 1) * 2;
+    const uint32_t sel = (uint32_t)b0 | ((uint32_t)(b0 + 4) << 8) | ((uint32_t)(b0 + 1) << 16) | ((uint32_t)(b0 + 5) << 24);
+    uint32_t lo4[4], hi4[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const uint32_t x = __builtin_amdgcn_perm(t.v[2 * qd + 1][word], t.v[2 * qd][word], sel);
+      lo4[qd] = fp8x2_to_bf16x2<false>(x);  // keys 2qd, 2qd+1 at d 8c + 2np
+      hi4[qd] = fp8x2_to_bf16x2<true>(x);   // same keys at d 8c + 2np + 1
+    }
+    const bf16x8 vb0 = __builtin_bit_cast(bf16x8, u32x4{lo4[0], lo4[1], lo4[2], lo4[3]});
+    const bf16x8 vb1 = __builtin_bit_cast(bf16x8, u32x4{hi4[0], hi4[1], hi4[2], hi4[3]});
+    o[0][2 * np] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa0, vb0, o[0][2 * np], 0, 0, 0);
+    o[1][2 * np] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa1, vb0, o[1][2 * np], 0, 0, 0);
+    o[0][2 * np + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa0, vb1, o[0][2 * np + 1], 0, 0, 0);
+    o[1][2 * np + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa1, vb1, o[1][2 * np + 1], 0, 0, 0);
+  }
+  if (more) xload_v(t, a, sp, k_next);
+  hook();
+}
+
+// Q of an item as the B operands of the score product: for column tile t and d step
+// s, lane l holds column c = l % 16 at d = 32s + 8g + e: tile 0 column c < 8 = hi of
+// head c, c >= 8 = mid of head c - 8; tile 1 column c < 8 = lo of head c, else 0.
+__device__ __forceinline__ void xqueries(const float (&qraw)[32], float qscale, int lane, bf16x8* qs) {
+  const int c = lane & 15;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    uint32_t w0[4], w1[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      float h0, m0, l0, h1, m1, l1;
+      split3(qraw[8 * st + 2 * qd] * qscale, h0, m0, l0);
+      split3(qraw[8 * st + 2 * qd + 1] * qscale, h1, m1, l1);
+      w0[qd] = c < 8 ? bf16_pair_of(h0, h1) : bf16_pair_of(m0, m1);
+      w1[qd] = c < 8 ? bf16_pair_of(l0, l1) : 0u;
+    }
+    qs[(0 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
+    qs[(1 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
+  }
+}
+
 #ifndef TL_DECODE_WAVES
 #define TL_DECODE_WAVES 4
 #endif
@@ -408,10 +648,10 @@ __device__ __forceinline__ Item item_of(const DecodeArgs& a, const ItemTables& t
 // entries of the split (one per lane; a split spans at most 64 pages) and the raw
 // queries.  They are only loaded here; the scale is applied when the item starts, so
 // loads issued for the next item are not waited on before then.
-template <int D>
+template <int NQR>
 struct ItemOps {
   int tab;
-  float q[D / 8];
+  float q[NQR];
 };
 
 // first q head of this lane's slot, and whether the lane's head exists
@@ -428,20 +668,34 @@ __device__ __forceinline__ void item_heads(const DecodeArgs& a, int y, int lane,
   }
 }
 
-template <int D, int G>
-__device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane, ItemOps<D>& op) {
+template <int D, int G, bool XP>
+__device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane,
+                                         ItemOps<XP ? 32 : D / 8>& op) {
   const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
   op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + min(first_block + lane, a.max_blocks - 1)];
-  int qh_base;
-  bool head_on;
-  item_heads<G>(a, it.y, lane, qh_base, head_on);
-  // register t of lane (slot, kg, j) holds Q[head j][d = 8t + kg], read from a valid
-  // head whatever the lane (an absent head is zeroed by its scale)
-  const int kg = (lane >> 2) & 7, j = lane & 3;
-  const int hq = min(qh_base + j, a.num_q_heads - 1);
-  const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + hq) * D + kg;
+  if constexpr (XP) {
+    // lane (c, g): head c % 8 of the group, d = 32s + 8g .. +7 for s = 0..3
+    const int c = lane & 15, g = lane >> 4;
+    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * 8 + (c & 7)) * D + 8 * g;
 #pragma unroll
-  for (int t = 0; t < D / 8; ++t) op.q[t] = qp[8 * t];
+    for (int st = 0; st < 4; ++st) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * st);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * st + 4);
+      op.q[8 * st + 0] = x0.x; op.q[8 * st + 1] = x0.y; op.q[8 * st + 2] = x0.z; op.q[8 * st + 3] = x0.w;
+      op.q[8 * st + 4] = x1.x; op.q[8 * st + 5] = x1.y; op.q[8 * st + 6] = x1.z; op.q[8 * st + 7] = x1.w;
+    }
+  } else {
+    int qh_base;
+    bool head_on;
+    item_heads<G>(a, it.y, lane, qh_base, head_on);
+    // register t of lane (slot, kg, j) holds Q[head j][d = 8t + kg], read from a valid
+    // head whatever the lane (an absent head is zeroed by its scale)
+    const int kg = (lane >> 2) & 7, j = lane & 3;
+    const int hq = min(qh_base + j, a.num_q_heads - 1);
+    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + hq) * D + kg;
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) op.q[t] = qp[8 * t];
+  }
 }
 
 // Persistent workgroups of NWD waves.  For each claimed item, wave w takes the
@@ -450,7 +704,7 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
 // on which workgroup ran it or when.  Item numbers are claimed two items ahead, and
 // each wave issues the next item's table entries and queries together with the loads
 // of its last tile of the current item, so a new item starts without waiting.
-template <int KVT, int D, int G>
+template <int KVT, int D, int G, bool XP>
 __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kernel(DecodeArgs a) {
   using GE = Geo<KVT, D>;
   constexpr int NT = GE::NT;
@@ -470,6 +724,7 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
   __shared__ int c_carry[1 + NBKT], c_wsum[NWD][1 + NBKT], s_claim[1];
   __shared__ float c_acc[NWD][NT * 4][64];    // [wave][value i*4 + r][lane]
   __shared__ float c_m[NWD][8], c_l[NWD][8];  // [wave][slot*4 + head]
+  __shared__ bf16x8 x_q[XP ? NWD : 1][XP ? 8 * 64 : 1];  // exact-split path: Q3 operands per wave
 
   // ---- numbering tables (inclusive block scans over the batch, NTHR at a time)
   if (tid <= NBKT) c_carry[tid] = 0;
@@ -526,8 +781,8 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
   int cur = blockIdx.x, nxt = blockIdx.x + n_wg;
   if (cur >= n_items) return;  // workgroup-uniform
   Item it = item_of(a, tabs, cur, gy);
-  ItemOps<D> op, nop;
-  item_ops<D, G>(a, it, lane, op);
+  ItemOps<XP ? 32 : D / 8> op, nop;
+  item_ops<D, G, XP>(a, it, lane, op);
   Item nit = it;
   if (nxt < n_items) nit = item_of(a, tabs, nxt, gy);
 
@@ -545,8 +800,10 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
       kvh = it.y * 2 + slot; slot_on = kvh < H; qh_base = kvh * G;
       if (!slot_on) kvh = H - 1;  // keep addresses valid; results are discarded
     }
-    float q[D / 8];
-    {
+    float q[XP ? 1 : D / 8];
+    if constexpr (XP) {
+      xqueries(op.q, a.qscale, lane, &x_q[w][0]);  // scores come out in log2 units
+    } else {
       int qb;
       bool head_on;
       item_heads<G>(a, it.y, lane, qb, head_on);
@@ -562,46 +819,79 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
     sp.first_block = (it.split * a.split_keys) >> a.pool.page_shift;
     sp.tab = clampi(op.tab, 0, a.pool.num_pages - 1);
 
-    v4f o[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) o[i] = v4f{0, 0, 0, 0};
     float m = -INFINITY, l = 0.0f;
-
-    // K of the wave's next tile is prefetched into the other buffer where registers
-    // allow it (fp8, D = 64); otherwise each tile loads its own K.  The wave's last
-    // tile is peeled so the next item's operands load with it.
     const bool has_next = nxt < n_items;
-    auto next_ops = [&]() { if (has_next) item_ops<D, G>(a, nit, lane, nop); };
-    KBuf<KVT, D> kA, kB;
-    VBuf<KVT, D> vA, vB_;
-    VBuf<KVT, D>& vB = (PF >= 2) ? vB_ : vA;  // one V buffer unless V is prefetched
+    auto next_ops = [&]() { if (has_next) item_ops<D, G, XP>(a, nit, lane, nop); };
     int k0 = k_begin + w * TK;
-    int par = 0;
-    if (k0 <= k_end) {
-      if constexpr (PF >= 1) load_k<KVT, D>(kA, a, sp, k0);
-      if constexpr (PF >= 2) load_v<KVT, D>(vA, a, sp, k0);
-      while (k0 + STEP <= k_end) {
-        decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l);
-        k0 += STEP;
-        if (k0 + STEP > k_end) { par = 1; break; }
-        decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l);
-        k0 += STEP;
+    if constexpr (XP) {
+      v4f ox[2][8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) ox[t][n] = v4f{0, 0, 0, 0};
+      XBuf xb;
+      const bf16x8* qsw = &x_q[w][0];
+      if (k0 <= k_end) {
+        xload(xb, a, sp, k0);
+        while (k0 + STEP <= k_end) {
+          xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l);
+          k0 += STEP;
+        }
+        xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l, next_ops);
+      } else {
+        next_ops();
       }
-      if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, next_ops);
-      else decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l, next_ops);
+      // ---- l over the lane groups; O = hi rows + mid rows (lanes + 32) + lo rows; to LDS
+      l = wave_xor_sum(l, 16);
+      l = wave_xor_sum(l, 32);
+      const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = (ox[0][n][r] + __shfl_xor(ox[0][n][r], 32, 64)) + ox[1][n][r];
+          if (g < 2) {
+            const int d = 8 * c + n;  // head 4g + r
+            c_acc[w][(d & 3) * 4 + r][g * 32 + (d >> 2)] = v;
+          }
+        }
+      if (lane < 8) { c_m[w][lane] = m; c_l[w][lane] = l; }
     } else {
-      next_ops();
+      v4f o[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) o[i] = v4f{0, 0, 0, 0};
+      // K of the wave's next tile is prefetched into the other buffer where registers
+      // allow it; otherwise each tile loads its own K.  The wave's last tile is peeled
+      // so the next item's operands load with it.
+      KBuf<KVT, D> kA, kB;
+      VBuf<KVT, D> vA, vB_;
+      VBuf<KVT, D>& vB = (PF >= 2) ? vB_ : vA;  // one V buffer unless V is prefetched
+      int par = 0;
+      if (k0 <= k_end) {
+        if constexpr (PF >= 1) load_k<KVT, D>(kA, a, sp, k0);
+        if constexpr (PF >= 2) load_v<KVT, D>(vA, a, sp, k0);
+        while (k0 + STEP <= k_end) {
+          decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l);
+          k0 += STEP;
+          if (k0 + STEP > k_end) { par = 1; break; }
+          decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l);
+          k0 += STEP;
+        }
+        if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, next_ops);
+        else decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l, next_ops);
+      } else {
+        next_ops();
+      }
+      // ---- l per head summed over the slot's key groups; the wave's state to LDS
+      l = wave_xor_sum(l, 4);
+      l = wave_xor_sum(l, 8);
+      l = wave_xor_sum(l, 16);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c_acc[w][i * 4 + r][lane] = o[i][r];
+      if (kg == 0) { c_m[w][slot * 4 + j] = m; c_l[w][slot * 4 + j] = l; }
     }
-
-    // ---- l per head summed over the slot's key groups; the wave's state to LDS
-    l = wave_xor_sum(l, 4);
-    l = wave_xor_sum(l, 8);
-    l = wave_xor_sum(l, 16);
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) c_acc[w][i * 4 + r][lane] = o[i][r];
-    if (kg == 0) { c_m[w][slot * 4 + j] = m; c_l[w][slot * 4 + j] = l; }
     if (tid == 0) s_claim[0] = claimed;
     __syncthreads();
 
@@ -731,15 +1021,24 @@ int resident_workgroups(K kernel, size_t dyn_lds) {
   return cached;
 }
 
-template <int KVT, int D, int G>
-hipError_t decode_launch_split(const DecodeArgs& a, hipStream_t s) {
+template <int KVT, int D, int G, bool XP>
+hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
   const int H = a.pool.num_kv_heads;
   const int64_t gy = (G == 8) ? H : (H + 1) / 2;
   const size_t dyn = (size_t)TABLE_INTS * a.batch * sizeof(int);
   const int64_t upper = (int64_t)a.batch * a.n_split * gy;
-  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups(decode_split_kernel<KVT, D, G>, dyn));
-  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G>), dim3((unsigned)wgs), dim3(NTHR), dyn, s, a);
+  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups(decode_split_kernel<KVT, D, G, XP>, dyn));
+  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP>), dim3((unsigned)wgs), dim3(NTHR), dyn, s, a);
   return hipGetLastError();
+}
+
+template <int KVT, int D, int G>
+hipError_t decode_launch_split(const DecodeArgs& a, hipStream_t s) {
+  // the exact bf16-split tile serves fp8 pools at D = 128, G = 8 with pages of >= 16
+  if constexpr (KVT == KV_FP8 && D == 128 && G == 8) {
+    if (a.pool.page_size >= 16) return decode_launch_split_x<KVT, D, G, true>(a, s);
+  }
+  return decode_launch_split_x<KVT, D, G, false>(a, s);
 }
 
 template <int KVT, int D>
