@@ -612,9 +612,16 @@ struct ItemTables {
 };
 constexpr int TABLE_INTS = 2 + NBKT;  // ints of LDS per sequence
 
-// Item number -> (sequence, head group, split).  Workgroup-uniform.
+// Item number -> (sequence, head group, split).  Workgroup-uniform (made scalar).
 struct Item { int b, y, split; };
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTables& t, int it, int gy);
 __device__ __forceinline__ Item item_of(const DecodeArgs& a, const ItemTables& t, int it, int gy) {
+  Item r = item_of_lds(a, t, uni(it), gy);
+  r.b = uni(r.b); r.y = uni(r.y); r.split = uni(r.split);
+  return r;
+}
+__device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTables& t, int it, int gy) {
   Item r;
   const int n = a.batch;
   int pair = it / gy;
@@ -775,7 +782,7 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
   int n_pairs = tabs.full[a.batch - 1];
 #pragma unroll
   for (int k = 0; k < NBKT; ++k) n_pairs += tabs.bkt[k][a.batch - 1];
-  const int n_items = n_pairs * gy;
+  const int n_items = uni(n_pairs * gy);
   // the first two items of each workgroup are fixed; later ones come from the counter
   const int n_wg = gridDim.x;
   int cur = blockIdx.x, nxt = blockIdx.x + n_wg;
@@ -811,7 +818,7 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
 #pragma unroll
       for (int t = 0; t < D / 8; ++t) q[t] = op.q[t] * qs;
     }
-    const SeqSplits ss = seq_splits(a, tabs.len[it.b]);
+    const SeqSplits ss = seq_splits(a, uni(tabs.len[it.b]));
     const int k_begin = max(it.split * a.split_keys, ss.lo) & ~(TK - 1);
     const int k_end = min((it.split + 1) * a.split_keys - 1, ss.hi);  // inclusive
     Split sp;
@@ -1066,10 +1073,10 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
 int decode_split_keys(int kv_dtype, int group, int page_size) {
   (void)group;
 #ifndef TL_DECODE_SPLIT_FP8
-#define TL_DECODE_SPLIT_FP8 1024
+#define TL_DECODE_SPLIT_FP8 4096
 #endif
 #ifndef TL_DECODE_SPLIT_OTHER
-#define TL_DECODE_SPLIT_OTHER 512
+#define TL_DECODE_SPLIT_OTHER 1024
 #endif
   const int want = kv_dtype == KV_FP8 ? TL_DECODE_SPLIT_FP8 : TL_DECODE_SPLIT_OTHER;
   return want < 64 * page_size ? want : 64 * page_size;  // a split spans at most 64 pages
