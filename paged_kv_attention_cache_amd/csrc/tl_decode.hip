@@ -308,19 +308,23 @@ __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp
 // Per wave and 32-key tile of one KV head (lane l, c = l % 16, g = l / 16):
 //   scores  S^T[key, col] = sum_d K[key, d] Q3[col, d]: two 16-key halves x two
 //           column tiles (columns: hi and mid of heads 0-7, then lo of heads 0-7 and
-//           8 zero columns) x four 32-wide d steps = 16 MFMAs.  Lane l then holds,
-//           for head c (c < 8), keys 16*h + 4g + r of the tile (h = half, r = 0..3).
+//           8 zero columns) x four 32-wide d steps = 16 MFMAs.  In step s the MFMA
+//           index k = 8g + e stands for d = 32g + 8s + e, so a lane's K bytes for
+//           the four steps are its key's two contiguous 16-byte chunks 2g, 2g+1.
+//           Lane l then holds, for head c (c < 8), keys 16*h + 4g + r of the tile
+//           (h = half, r = 0..3).
 //   values  O3[row, d] += sum_key P3[row, key] V[key, d]: rows are hi and mid of
 //           heads 0-7 (tile 0) and lo (tile 1); d = 8c + n for d tile n = 0..7; the
 //           key order of the sum is that of the score lanes (key 16*(e/4) + 4g + e%4
 //           for k = 8g + e), so P stays in the lane that computed it: 16 MFMAs.
-// Per lane per tile: 8 K loads and 8 V loads of 8 bytes, no value loaded twice.
+// Per lane per tile: 4 K loads of 16 bytes, 8 V loads of 8 bytes and 4 scale loads;
+// no value is loaded twice.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct XBuf {
-  u32x2 k[2][4];  // [half][d step]: 8 fp8 of key 16*half + c at d 32s + 8g .. +7
+  u32x4 k[2][2];  // [half][chunk]: 16 fp8 of key 16*half + c at d 32g + 16j .. +15
   u32x2 v[8];     // [e]: 8 fp8 of key 16*(e/4) + 4g + e%4 at d 8c .. 8c+7
   v4f ks[2], vs[2];  // [half]: scales of keys 16*half + 4g .. +3
 };
@@ -366,13 +370,11 @@ __device__ __forceinline__ void xload_k(XBuf& t, const DecodeArgs& a, const Spli
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const XHalf x = xhalf(a, sp, k0, h);
-    // key clamped into [lo, hi]; chunk 2s + g/2, byte half g%2
+    // key clamped into [lo, hi]; chunks 2g and 2g + 1 (d 32g .. 32g + 31)
     const int key = clampi(x.hk0 + c, sp.lo, sp.hi);
-    const unsigned char* kb = reinterpret_cast<const unsigned char*>(a.pool.k) +
-                              ((x.ph * NC + (g >> 1)) * S + (key & (S - 1))) * 16 + 8 * (g & 1);
+    const uint4* kb = reinterpret_cast<const uint4*>(a.pool.k) + (x.ph * NC + 2 * g) * S + (key & (S - 1));
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      t.k[h][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kb + (int64_t)2 * st * S * 16));
+    for (int j = 0; j < 2; ++j) t.k[h][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)j * S));
   }
 }
 __device__ __forceinline__ void xload_scales(XBuf& t, const DecodeArgs& a, const Split& sp, int k0, bool kside) {
@@ -426,11 +428,12 @@ __device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf
     v4f t0 = v4f{0, 0, 0, 0}, t1 = v4f{0, 0, 0, 0};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      const uint32_t d0 = t.k[h][st >> 1][2 * (st & 1)], d1 = t.k[h][st >> 1][2 * (st & 1) + 1];
       uint32_t w[4];
-      w[0] = fp8x2_to_bf16x2<false>(t.k[h][st][0]);
-      w[1] = fp8x2_to_bf16x2<true>(t.k[h][st][0]);
-      w[2] = fp8x2_to_bf16x2<false>(t.k[h][st][1]);
-      w[3] = fp8x2_to_bf16x2<true>(t.k[h][st][1]);
+      w[0] = fp8x2_to_bf16x2<false>(d0);
+      w[1] = fp8x2_to_bf16x2<true>(d0);
+      w[2] = fp8x2_to_bf16x2<false>(d1);
+      w[3] = fp8x2_to_bf16x2<true>(d1);
       const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qs[(0 * 4 + st) * 64 + sp.lane], t0, 0, 0, 0);
       t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qs[(1 * 4 + st) * 64 + sp.lane], t1, 0, 0, 0);
@@ -515,7 +518,7 @@ __device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf
 }
 
 // Q of an item as the B operands of the score product: for column tile t and d step
-// s, lane l holds column c = l % 16 at d = 32s + 8g + e: tile 0 column c < 8 = hi of
+// s, lane l holds column c = l % 16 at d = 32g + 8s + e: tile 0 column c < 8 = hi of
 // head c, c >= 8 = mid of head c - 8; tile 1 column c < 8 = lo of head c, else 0.
 __device__ __forceinline__ void xqueries(const float (&qraw)[32], float qscale, int lane, bf16x8* qs) {
   const int c = lane & 15;
@@ -544,7 +547,9 @@ constexpr int NTHR = 64 * NWD;
 #define TL_DECODE_MIN_WAVES 2
 #endif
 // waves per SIMD the register budget is sized for (f32 tiles need twice the registers)
-template <int KVT> struct DecodeOcc { static constexpr int value = KVT == KV_F32 ? 1 : TL_DECODE_MIN_WAVES; };
+template <int KVT, bool XP> struct DecodeOcc {
+  static constexpr int value = KVT == KV_F32 ? 1 : TL_DECODE_MIN_WAVES;
+};
 
 // ---------------------------------------------------------------- work items
 // A work item is one split of one sequence for one head group.  Items are numbered
@@ -681,13 +686,13 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
   const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
   op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + min(first_block + lane, a.max_blocks - 1)];
   if constexpr (XP) {
-    // lane (c, g): head c % 8 of the group, d = 32s + 8g .. +7 for s = 0..3
+    // lane (c, g): head c % 8 of the group, d = 32g + 8s .. +7 for s = 0..3
     const int c = lane & 15, g = lane >> 4;
-    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * 8 + (c & 7)) * D + 8 * g;
+    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * 8 + (c & 7)) * D + 32 * g;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * st);
-      const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * st + 4);
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + 8 * st);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 8 * st + 4);
       op.q[8 * st + 0] = x0.x; op.q[8 * st + 1] = x0.y; op.q[8 * st + 2] = x0.z; op.q[8 * st + 3] = x0.w;
       op.q[8 * st + 4] = x1.x; op.q[8 * st + 5] = x1.y; op.q[8 * st + 6] = x1.z; op.q[8 * st + 7] = x1.w;
     }
@@ -712,7 +717,7 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
 // each wave issues the next item's table entries and queries together with the loads
 // of its last tile of the current item, so a new item starts without waiting.
 template <int KVT, int D, int G, bool XP>
-__global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_split_kernel(DecodeArgs a) {
   using GE = Geo<KVT, D>;
   constexpr int NT = GE::NT;
   constexpr int PF = DecodePrefetch<KVT, D, G>::value;
@@ -836,8 +841,8 @@ __global__ __launch_bounds__(NTHR, DecodeOcc<KVT>::value) void decode_split_kern
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int n = 0; n < 8; ++n) ox[t][n] = v4f{0, 0, 0, 0};
-      XBuf xb;
       const bf16x8* qsw = &x_q[w][0];
+      XBuf xb;
       if (k0 <= k_end) {
         xload(xb, a, sp, k0);
         while (k0 + STEP <= k_end) {
