@@ -562,14 +562,14 @@ template <int KVT, bool XP> struct DecodeOcc {
 // numbering in LDS from the lengths (prefix sums over the batch).
 constexpr int NBKT = 4;
 
-struct SeqSplits { int lo, hi, s_first, s_last, f_first, f_last, nf, part[2], np; };
+struct SeqSplits { int lo, hi, s_first, s_last, f_first, f_last, nf, p0, p1, np; };  // partial splits p0, p1 (np of them)
 
 __device__ __forceinline__ SeqSplits seq_splits(const DecodeArgs& a, int L) {
   SeqSplits r;
   const int sk = a.split_keys;
   L = min(L, a.max_blocks * a.pool.page_size);
   r.np = 0;
-  r.part[0] = r.part[1] = 0;
+  r.p0 = r.p1 = 0;
   if (L <= 0) {
     r.lo = 0; r.hi = -1; r.s_first = 0; r.s_last = -1; r.f_first = 0; r.f_last = -1; r.nf = 0;
     return r;
@@ -581,8 +581,12 @@ __device__ __forceinline__ SeqSplits seq_splits(const DecodeArgs& a, int L) {
   r.f_first = (r.lo + sk - 1) / sk;  // first split wholly inside [lo, hi]
   r.f_last = (r.hi + 1) / sk - 1;    // last one
   r.nf = max(0, r.f_last - r.f_first + 1);
-  if (r.s_first < r.f_first || r.s_first > r.f_last) r.part[r.np++] = r.s_first;
-  if (r.s_last != r.s_first && (r.s_last < r.f_first || r.s_last > r.f_last)) r.part[r.np++] = r.s_last;
+  // (no run-time array indexing here: such arrays would live in scratch memory)
+  const bool first_partial = r.s_first < r.f_first || r.s_first > r.f_last;
+  const bool last_partial = r.s_last != r.s_first && (r.s_last < r.f_first || r.s_last > r.f_last);
+  r.np = (int)first_partial + (int)last_partial;
+  r.p0 = first_partial ? r.s_first : r.s_last;
+  r.p1 = r.s_last;
   return r;
 }
 
@@ -647,12 +651,10 @@ __device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTable
   r.b = lds_upper(t.bkt[k], n, pair);
   const SeqSplits ss = seq_splits(a, t.len[r.b]);
   const int before = t.bkt[k][r.b] - (r.b > 0 ? t.bkt[k][r.b - 1] : 0);  // this sequence's count in k
-  int local = pair - (t.bkt[k][r.b] - before);
-  r.split = ss.part[0];
-  for (int u = 0; u < ss.np; ++u) {
-    if (tile_bucket(a, split_tiles(a, ss, ss.part[u])) != k) continue;
-    if (local-- == 0) { r.split = ss.part[u]; break; }
-  }
+  const int local = pair - (t.bkt[k][r.b] - before);
+  // the local-th of this sequence's partial splits that fall in bucket k
+  const bool in0 = ss.np > 0 && tile_bucket(a, split_tiles(a, ss, ss.p0)) == k;
+  r.split = (in0 && local == 0) ? ss.p0 : ss.p1;
   return r;
 }
 
@@ -750,7 +752,10 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
       const int L = a.seq_lens[b];
       const SeqSplits ss = seq_splits(a, L);
       cnt[0] = ss.nf;
-      for (int u = 0; u < ss.np; ++u) cnt[1 + tile_bucket(a, split_tiles(a, ss, ss.part[u]))] += 1;
+      const int b0 = ss.np > 0 ? tile_bucket(a, split_tiles(a, ss, ss.p0)) : -1;
+      const int b1 = ss.np > 1 ? tile_bucket(a, split_tiles(a, ss, ss.p1)) : -1;
+#pragma unroll
+      for (int k = 0; k < NBKT; ++k) cnt[1 + k] = (int)(b0 == k) + (int)(b1 == k);
       tabs.len[b] = L;
     }
 #pragma unroll
@@ -836,11 +841,15 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
     auto next_ops = [&]() { if (has_next) item_ops<D, G, XP>(a, nit, lane, nop); };
     int k0 = k_begin + w * TK;
     if constexpr (XP) {
+      // accumulators start from a zero made inside the item loop, so the compiler
+      // does not keep 64 zero registers live (or spilled) across it
+      float zero;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
       v4f ox[2][8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) ox[t][n] = v4f{0, 0, 0, 0};
+        for (int n = 0; n < 8; ++n) ox[t][n] = v4f{zero, zero, zero, zero};
       const bf16x8* qsw = &x_q[w][0];
       XBuf xb;
       if (k0 <= k_end) {
