@@ -87,6 +87,8 @@ def run_config(name: str, steps: int, warmup: int):
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_step = wall * 1e3 / steps
 
+    hist_write = history_write_rate(wl, pool) if wl.kind == "decode" else None
+
     if wl.kind == "decode":
         attn_bytes = A.decode_bytes(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size,
                                     wl.kv_dtype, wl.window)
@@ -100,6 +102,7 @@ def run_config(name: str, steps: int, warmup: int):
             "flops": A.decode_flops(wl.seq_lens, wl.num_q_heads, wl.head_dim, wl.window),
         }
         res["hbm_frac"] = res["attn_GBps"] / HBM_PEAK_GBPS
+        res.update(hist_write)
     else:
         pos = wl.row_positions()
         flops = A.prefill_flops(pos, wl.num_q_heads, wl.head_dim, wl.window)
@@ -115,6 +118,31 @@ def run_config(name: str, steps: int, warmup: int):
     del step, pool
     torch.cuda.empty_cache()
     return wl, res
+
+
+def history_write_rate(wl, pool, reps: int = 10):
+    """KV_CACHE_WRITE throughput on the workload's first history chunk (up to 64K tokens):
+    the same rows rewritten to the same slots, timed with HIP events."""
+    import torch
+    from paged_kv_attention_cache_amd import accounting as A
+    from paged_kv_attention_cache_amd import runner as R
+    from paged_kv_attention_cache_amd import tl_kv_cache_write
+    k, v, slots = next(wl.history_batches())
+    dk, dv, ds = R._t(k, "cuda"), R._t(v, "cuda"), R._t(slots, "cuda")
+    for _ in range(2):
+        tl_kv_cache_write(pool, dk, dv, ds)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        tl_kv_cache_write(pool, dk, dv, ds)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = A.write_bytes(slots, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    return {"hist_write_tokens": int(len(slots)), "hist_write_bytes": nbytes, "hist_write_ms": ms,
+            "hist_write_GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
 def cpu_baseline(target_s: float = 12.0, cap_s: float = 30.0):

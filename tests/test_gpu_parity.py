@@ -217,6 +217,37 @@ def test_decode_batch_invariance_bitwise(torch_cuda):
         assert torch.equal(one[0], full[b]), f"sequence {b} differs alone vs in batch"
 
 
+def test_decode_workspace_reused_across_calls(torch_cuda):
+    """One zero-filled workspace serves later calls of other shapes: each call leaves its
+    work counter at zero, and every result equals the one from a fresh workspace."""
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    cases = [W.custom_decode(440, [1500, 77, 3000, 515], 16, 2, 128, 16, "bf16"),
+             W.custom_decode(441, [9000, 64, 4097], 16, 2, 128, 64, "fp8"),
+             W.custom_decode(442, [33, 700], 8, 2, 64, 16, "f32", window=300)]
+    steps = []
+    for wl in cases:
+        gp = R.make_pool(wl)
+        R.write_history(gp, wl)
+        st = R.DecodeStep(wl, gp)
+        st.write()
+        steps.append((wl, gp, st))
+    need = max(tl.tl_paged_attn_decode_workspace_size(gp, wl.batch, wl.num_q_heads, wl.max_blocks)
+               for wl, gp, _ in steps)
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    fresh = []
+    for wl, gp, st in steps:
+        fresh.append(tl.tl_paged_attn_decode(gp, st.q, st.tables, st.seq_lens, wl.window, wl.scale).clone())
+    for rnd in range(2):
+        for i, (wl, gp, st) in enumerate(steps):
+            out = tl.tl_paged_attn_decode(gp, st.q, st.tables, st.seq_lens, wl.window, wl.scale, workspace=shared)
+            torch.cuda.synchronize()
+            assert torch.equal(out, fresh[i]), f"case {i} round {rnd}: reused workspace changes the result"
+            nb = tl.tl_paged_attn_decode_workspace_size(gp, wl.batch, wl.num_q_heads, wl.max_blocks)
+            ctrl = shared[nb - 16:nb - 12].cpu().numpy().view(np.int32)[0]
+            assert ctrl == 0, f"work counter left at {ctrl}"
+
+
 # ===================================================================== prefill
 PREFILL_CASES = [
     # (name, row_lens, start_pos, T, Hq, Hkv, D, S, dtype, window)
