@@ -3,10 +3,12 @@
 // whose KV is never written, section 1).  Also the test gather that copies a
 // sequence's stored rows out in logical order.
 //
-// Mapping: 8 lanes own one (token, kv head) row of D values, each lane D/8
-// contiguous values, so a wave reads 8 consecutive rows = one contiguous span of
-// k_new.  The stored encodings are those of include/tl.h.  HBM-bound: each row is
-// read once in f32 and written once in the pool dtype.
+// Mapping: 8 lanes own one (token, kv head) row of D values; the 8 rows of a wave
+// are 8 consecutive tokens of one head, and each lane holds whole 16-byte store
+// units of the encoded row, interleaved across the 8 lanes, so every store
+// instruction writes whole lines of the K and V pages when slots are consecutive.
+// The stored encodings are those of include/tl.h.  HBM-bound: each row is read
+// once in f32 and written once in the pool dtype.
 #include "tl_internal.h"
 
 namespace tl {
@@ -14,90 +16,135 @@ namespace {
 
 constexpr int ROW_LANES = 8;
 constexpr int WG = 256;
+typedef unsigned int wu4 __attribute__((ext_vector_type(4)));
+typedef unsigned int wu2 __attribute__((ext_vector_type(2)));
 
+// Every byte is read or written once.  Measured on a 62.5K-token bf16 history chunk
+// and a 52K-token fp8 one: f32/bf16 pools stream best with nontemporal loads and
+// plain stores, fp8 pools (a quarter of the bytes written, more arithmetic per byte)
+// with plain loads and nontemporal stores.
+template <bool NT, typename V>
+__device__ __forceinline__ void wst(V x, V* p) {
+  if constexpr (NT) __builtin_nontemporal_store(x, p); else *p = x;
+}
+template <bool NT>
+__device__ __forceinline__ wu4 wld(const wu4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
+}
+
+template <int KVT, int D>
+__device__ __forceinline__ void encode_row(const float (&x)[D / ROW_LANES], typename KvTraits<KVT>::T (&enc)[D / ROW_LANES],
+                                           float& scale) {
+  using Tr = KvTraits<KVT>;
+  constexpr int E = D / ROW_LANES;
+  scale = 1.0f;
+  if constexpr (KVT == KV_F32) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) enc[i] = x[i];
+  } else if constexpr (KVT == KV_BF16) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) enc[i] = (uint16_t)f32_to_bf16(x[i]);
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(x[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    scale = (m == 0.0f) ? 1.0f : m / 448.0f;  // IEEE f32 divide
+#pragma unroll
+    for (int i = 0; i < E; i += 2) {
+      float y0 = fminf(fmaxf(x[i] / scale, -448.0f), 448.0f);
+      float y1 = fminf(fmaxf(x[i + 1] / scale, -448.0f), 448.0f);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      enc[i] = (uint8_t)(w & 0xFF);
+      enc[i + 1] = (uint8_t)((w >> 8) & 0xFF);
+    }
+  }
+  (void)sizeof(Tr);
+}
+
+// Rows are (token, kv head) pairs, ordered so that the 8 rows of a wave's lane group
+// are 8 consecutive tokens of one head: their K chunks and V rows then land next to
+// each other in the pool when their slots are consecutive (history writes).  Every
+// byte is read or written once, so loads and stores are nontemporal.
 template <int KVT, int D>
 __global__ __launch_bounds__(WG) void write_kernel(WriteArgs a) {
   using Tr = KvTraits<KVT>;
+  typedef typename Tr::T T;
+  typedef wu4 u4;
+  typedef wu2 u2;
   constexpr int E = D / ROW_LANES;   // values per lane
   constexpr int X = Tr::X;           // values per 16-byte chunk
   constexpr int NC = D / X;          // chunks per row
   const int lane_in_row = threadIdx.x % ROW_LANES;
-  const int64_t row = (int64_t)blockIdx.x * (WG / ROW_LANES) + threadIdx.x / ROW_LANES;
+  const int64_t r = (int64_t)blockIdx.x * (WG / ROW_LANES) + threadIdx.x / ROW_LANES;
   const int H = a.pool.num_kv_heads;
-  const int64_t rows = a.n_tokens * H;
-  if (row >= rows) return;
-  const int64_t token = row / H;
-  const int h = (int)(row - token * H);
+  // r -> (token block of 8, head, token in block)
+  const int64_t blk = r / (8 * H);
+  const int h = (int)((r / 8) % H);
+  const int64_t token = blk * 8 + (r % 8);
+  if (token >= a.n_tokens) return;
   const int32_t slot = a.slots[token];
   const int64_t limit = (int64_t)a.pool.num_pages * a.pool.page_size;
   if (slot < 0 || slot >= limit) return;  // -1 is a pad; anything else out of range is skipped
   const int S = a.pool.page_size;
   const int page = slot >> a.pool.page_shift;
   const int off = slot & (S - 1);
-  const int d0 = lane_in_row * E;
-
-  for (int which = 0; which < 2; ++which) {
-    const float* src = (which == 0 ? a.k_new : a.v_new) + row * D + d0;
-    float x[E];
+  const int64_t row = token * H + h;
+  // A unit is UE consecutive values whose encoding is one store (16 bytes, or 8 for
+  // fp8 rows of 64); lane j of the row's 8 owns units j, j + 8, ... so that each store
+  // instruction of the 8 lanes covers one contiguous span of the destination.
+  constexpr int UE = (X * ROW_LANES <= D) ? X : D / ROW_LANES;
+  constexpr int NU = E / UE;  // units per lane
+  constexpr bool NTL = KVT != KV_FP8, NTS = KVT == KV_FP8;
+  float xk[E], xv[E];
+  {
+    const u4* sk = reinterpret_cast<const u4*>(a.k_new + row * D);
+    const u4* sv = reinterpret_cast<const u4*>(a.v_new + row * D);
 #pragma unroll
-    for (int i = 0; i < E; i += 4) {
-      float4 t = *reinterpret_cast<const float4*>(src + i);
-      x[i] = t.x; x[i + 1] = t.y; x[i + 2] = t.z; x[i + 3] = t.w;
-    }
-    typename Tr::T enc[E];
-    float scale = 1.0f;
-    if constexpr (KVT == KV_F32) {
+    for (int i = 0; i < NU; ++i) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) enc[i] = x[i];
-    } else if constexpr (KVT == KV_BF16) {
+      for (int q = 0; q < UE / 4; ++q) {
+        const int at = (UE * (lane_in_row + ROW_LANES * i)) / 4 + q;
+        const u4 tk = wld<NTL>(sk + at);
+        const u4 tv = wld<NTL>(sv + at);
 #pragma unroll
-      for (int i = 0; i < E; ++i) enc[i] = (uint16_t)f32_to_bf16(x[i]);
-    } else {
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(x[i]));
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      m = fmaxf(m, __shfl_xor(m, 2, 64));
-      m = fmaxf(m, __shfl_xor(m, 4, 64));
-      scale = (m == 0.0f) ? 1.0f : m / 448.0f;  // IEEE f32 divide
-#pragma unroll
-      for (int i = 0; i < E; i += 2) {
-        float y0 = fminf(fmaxf(x[i] / scale, -448.0f), 448.0f);
-        float y1 = fminf(fmaxf(x[i + 1] / scale, -448.0f), 448.0f);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-        enc[i] = (uint8_t)(w & 0xFF);
-        enc[i + 1] = (uint8_t)((w >> 8) & 0xFF);
-      }
-    }
-    typename Tr::T* base = reinterpret_cast<typename Tr::T*>(which == 0 ? a.k : a.v);
-    if (which == 0) {
-      // K: [page][h][D/X][S][X]; this lane's E values cover whole or half chunks
-#pragma unroll
-      for (int i = 0; i < E; i += (E < X ? E : X)) {
-        const int d = d0 + i;
-        const int c = d / X, e = d % X;
-        typename Tr::T* dst = base + ((((int64_t)page * H + h) * NC + c) * S + off) * X + e;
-        constexpr int W = (E < X ? E : X) * Tr::BYTES;
-        if constexpr (W == 16) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&enc[i]);
-        } else {
-          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&enc[i]);
+        for (int e = 0; e < 4; ++e) {
+          xk[i * UE + 4 * q + e] = __uint_as_float(tk[e]);
+          xv[i * UE + 4 * q + e] = __uint_as_float(tv[e]);
         }
       }
-    } else {
-      // V: [page][h][S][D], contiguous row
-      typename Tr::T* dst = base + (((int64_t)page * H + h) * S + off) * D + d0;
-      constexpr int BYTES = E * Tr::BYTES;
-#pragma unroll
-      for (int i = 0; i < BYTES / 16; ++i)
-        reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(enc)[i];
-      if constexpr (BYTES % 16 == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(enc);
     }
-    if constexpr (KVT == KV_FP8) {
-      if (lane_in_row == 0) {
-        float* sc = (which == 0 ? a.k_scale : a.v_scale);
-        sc[((int64_t)page * H + h) * S + off] = scale;
+  }
+  T ek[E], ev[E];
+  float sck, scv;
+  encode_row<KVT, D>(xk, ek, sck);
+  encode_row<KVT, D>(xv, ev, scv);
+  constexpr int W = UE * Tr::BYTES;
+  static_assert(W == 16 || W == 8, "unit is one 16- or 8-byte store");
+  {
+    T* kb = reinterpret_cast<T*>(a.k);
+    T* vrow = reinterpret_cast<T*>(a.v) + (((int64_t)page * H + h) * S + off) * D;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int d = UE * (lane_in_row + ROW_LANES * i);
+      const int c = d / X, e = d % X;
+      T* kd = kb + ((((int64_t)page * H + h) * NC + c) * S + off) * X + e;
+      if constexpr (W == 16) {
+        wst<NTS>(*reinterpret_cast<const u4*>(&ek[i * UE]), reinterpret_cast<u4*>(kd));
+        wst<NTS>(*reinterpret_cast<const u4*>(&ev[i * UE]), reinterpret_cast<u4*>(vrow + d));
+      } else {
+        wst<NTS>(*reinterpret_cast<const u2*>(&ek[i * UE]), reinterpret_cast<u2*>(kd));
+        wst<NTS>(*reinterpret_cast<const u2*>(&ev[i * UE]), reinterpret_cast<u2*>(vrow + d));
       }
+    }
+  }
+  if constexpr (KVT == KV_FP8) {
+    if (lane_in_row == 0) {
+      const int64_t si = ((int64_t)page * H + h) * S + off;
+      a.k_scale[si] = sck;
+      a.v_scale[si] = scv;
     }
   }
 }
@@ -142,7 +189,8 @@ __global__ __launch_bounds__(WG) void gather_kernel(GatherArgs a) {
 
 template <int KVT>
 hipError_t write_dispatch(const WriteArgs& a, hipStream_t s) {
-  const int64_t rows = a.n_tokens * a.pool.num_kv_heads;
+  // rows are counted in whole blocks of 8 tokens (the tail block's missing tokens return)
+  const int64_t rows = ((a.n_tokens + 7) / 8) * 8 * a.pool.num_kv_heads;
   const dim3 grid((unsigned)((rows + (WG / ROW_LANES) - 1) / (WG / ROW_LANES)));
   if (a.pool.head_dim == 128) hipLaunchKernelGGL((write_kernel<KVT, 128>), grid, dim3(WG), 0, s, a);
   else hipLaunchKernelGGL((write_kernel<KVT, 64>), grid, dim3(WG), 0, s, a);
