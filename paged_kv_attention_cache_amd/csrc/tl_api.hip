@@ -175,8 +175,9 @@ size_t tl_paged_attn_decode_workspace_size(const tl_kv_pool* pool, int32_t batch
   if (check_pool(fn, pool) || check_group(fn, pool, num_q_heads)) return 0;
   if (batch <= 0 || max_blocks <= 0) return 0;
   const int64_t ns = decode_nsplit(pool, num_q_heads, max_blocks);
-  // partial states (acc, then m and l) and 16 bytes of control words
-  return (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float) + 16;
+  // 16 bytes of control words (at offset 0 whatever the shape), then the partial
+  // states (acc, then m and l)
+  return 16 + (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float);
 }
 
 int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_heads, const int32_t* block_tables,
@@ -221,9 +222,9 @@ int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_h
   a.pool = pool_args(pool);
   a.q = q; a.block_tables = block_tables; a.seq_lens = seq_lens; a.out = out;
   const int64_t ns = decode_nsplit(pool, num_q_heads, max_blocks);
-  a.ws_acc = (float*)workspace;
+  a.ws_ctrl = reinterpret_cast<int*>(workspace);  // same place for every shape
+  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 16);
   a.ws_ml = a.ws_acc + (size_t)batch * num_q_heads * ns * pool->head_dim;
-  a.ws_ctrl = reinterpret_cast<int*>(a.ws_ml + (size_t)batch * num_q_heads * ns * 2);
   a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = max_blocks;
   a.batch = batch; a.window = window;
   a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->page_size);

@@ -520,22 +520,21 @@ __device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf
 // Q of an item as the B operands of the score product: for column tile t and d step
 // s, lane l holds column c = l % 16 at d = 32g + 8s + e: tile 0 column c < 8 = hi of
 // head c, c >= 8 = mid of head c - 8; tile 1 column c < 8 = lo of head c, else 0.
-__device__ __forceinline__ void xqueries(const float (&qraw)[32], float qscale, int lane, bf16x8* qs) {
+// The operands are shared by the workgroup's waves; each builds one step st from the
+// 8 raw values qraw = Q[head c % 8][32g + 8st .. +7].
+__device__ __forceinline__ void xqueries(const float (&qraw)[8], float qscale, int lane, int st, bf16x8* qs) {
   const int c = lane & 15;
+  uint32_t w0[4], w1[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    uint32_t w0[4], w1[4];
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      float h0, m0, l0, h1, m1, l1;
-      split3(qraw[8 * st + 2 * qd] * qscale, h0, m0, l0);
-      split3(qraw[8 * st + 2 * qd + 1] * qscale, h1, m1, l1);
-      w0[qd] = c < 8 ? bf16_pair_of(h0, h1) : bf16_pair_of(m0, m1);
-      w1[qd] = c < 8 ? bf16_pair_of(l0, l1) : 0u;
-    }
-    qs[(0 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
-    qs[(1 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
+  for (int qd = 0; qd < 4; ++qd) {
+    float h0, m0, l0, h1, m1, l1;
+    split3(qraw[2 * qd] * qscale, h0, m0, l0);
+    split3(qraw[2 * qd + 1] * qscale, h1, m1, l1);
+    w0[qd] = c < 8 ? bf16_pair_of(h0, h1) : bf16_pair_of(m0, m1);
+    w1[qd] = c < 8 ? bf16_pair_of(l0, l1) : 0u;
   }
+  qs[(0 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
+  qs[(1 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
 }
 
 #ifndef TL_DECODE_WAVES
@@ -556,8 +555,8 @@ template <int KVT, bool XP> struct DecodeOcc {
 // densely, longest first: every sequence's whole splits, then the partial ones (a
 // sequence's first split when the window cuts into it, its last when the length is
 // not a multiple of the split size) in NBKT buckets of decreasing tile count.
-// Workgroups are persistent and take items in that order (the first two statically,
-// then from a counter in the workspace), so the launch ends on its shortest items and
+// Workgroups are persistent and take items in that order (the first statically, then
+// from a counter in the workspace), so the launch ends on its shortest items and
 // no workgroup is spent on a split that does not exist.  Every workgroup rebuilds the
 // numbering in LDS from the lengths (prefix sums over the batch).
 constexpr int NBKT = 4;
@@ -683,21 +682,18 @@ __device__ __forceinline__ void item_heads(const DecodeArgs& a, int y, int lane,
 }
 
 template <int D, int G, bool XP>
-__device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane,
-                                         ItemOps<XP ? 32 : D / 8>& op) {
+__device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane, int w,
+                                         ItemOps<XP ? 8 : D / 8>& op) {
   const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
   op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + min(first_block + lane, a.max_blocks - 1)];
   if constexpr (XP) {
-    // lane (c, g): head c % 8 of the group, d = 32g + 8s .. +7 for s = 0..3
+    // lane (c, g) of wave w: head c % 8 of the group, d = 32g + 8w .. +7 (step w)
     const int c = lane & 15, g = lane >> 4;
-    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * 8 + (c & 7)) * D + 32 * g;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const float4 x0 = *reinterpret_cast<const float4*>(qp + 8 * st);
-      const float4 x1 = *reinterpret_cast<const float4*>(qp + 8 * st + 4);
-      op.q[8 * st + 0] = x0.x; op.q[8 * st + 1] = x0.y; op.q[8 * st + 2] = x0.z; op.q[8 * st + 3] = x0.w;
-      op.q[8 * st + 4] = x1.x; op.q[8 * st + 5] = x1.y; op.q[8 * st + 6] = x1.z; op.q[8 * st + 7] = x1.w;
-    }
+    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * 8 + (c & 7)) * D + 32 * g + 8 * w;
+    const float4 x0 = *reinterpret_cast<const float4*>(qp);
+    const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+    op.q[0] = x0.x; op.q[1] = x0.y; op.q[2] = x0.z; op.q[3] = x0.w;
+    op.q[4] = x1.x; op.q[5] = x1.y; op.q[6] = x1.z; op.q[7] = x1.w;
   } else {
     int qh_base;
     bool head_on;
@@ -715,9 +711,10 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
 // Persistent workgroups of NWD waves.  For each claimed item, wave w takes the
 // split's tiles w, w + NWD, ... with its own softmax state; the NWD states are then
 // combined through LDS in wave order, so the result depends on the split alone, not
-// on which workgroup ran it or when.  Item numbers are claimed two items ahead, and
-// each wave issues the next item's table entries and queries together with the loads
-// of its last tile of the current item, so a new item starts without waiting.
+// on which workgroup ran it or when.  The next item number is claimed as wave 0
+// starts its last tile of the current item (so an item goes to a workgroup only when
+// that workgroup is nearly free: longest-processing-time-first scheduling), and the
+// next item's table entries and queries load while the current item is combined.
 template <int KVT, int D, int G, bool XP>
 __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_split_kernel(DecodeArgs a) {
   using GE = Geo<KVT, D>;
@@ -738,7 +735,8 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
   __shared__ int c_carry[1 + NBKT], c_wsum[NWD][1 + NBKT], s_claim[1];
   __shared__ float c_acc[NWD][NT * 4][64];    // [wave][value i*4 + r][lane]
   __shared__ float c_m[NWD][8], c_l[NWD][8];  // [wave][slot*4 + head]
-  __shared__ bf16x8 x_q[XP ? NWD : 1][XP ? 8 * 64 : 1];  // exact-split path: Q3 operands per wave
+  __shared__ bf16x8 x_q[XP ? 8 * 64 : 1];  // exact-split path: Q3 operands of the item
+  static_assert(!XP || NWD == 4, "each of the 4 waves builds one d step of the exact-split queries");
 
   // ---- numbering tables (inclusive block scans over the batch, NTHR at a time)
   if (tid <= NBKT) c_carry[tid] = 0;
@@ -793,20 +791,22 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
 #pragma unroll
   for (int k = 0; k < NBKT; ++k) n_pairs += tabs.bkt[k][a.batch - 1];
   const int n_items = uni(n_pairs * gy);
-  // the first two items of each workgroup are fixed; later ones come from the counter
+  // the first item of each workgroup is fixed; later ones come from the counter
   const int n_wg = gridDim.x;
-  int cur = blockIdx.x, nxt = blockIdx.x + n_wg;
+  int cur = blockIdx.x;
   if (cur >= n_items) return;  // workgroup-uniform
   Item it = item_of(a, tabs, cur, gy);
-  ItemOps<XP ? 32 : D / 8> op, nop;
-  item_ops<D, G, XP>(a, it, lane, op);
-  Item nit = it;
-  if (nxt < n_items) nit = item_of(a, tabs, nxt, gy);
+  ItemOps<XP ? 8 : D / 8> op;
+  item_ops<D, G, XP>(a, it, lane, w, op);
+  if constexpr (XP) xqueries(op.q, a.qscale, lane, w, x_q);  // scores come out in log2 units
 
   for (;;) {
     __syncthreads();  // the previous item's combine is done everywhere
     int claimed = 0;
-    if (tid == 0) claimed = 2 * n_wg + atomicAdd(a.ws_ctrl, 1);  // the item after nxt
+    // The next item is claimed when wave 0 starts its last tile of this one, so items
+    // go to workgroups in the order they become free (longest first), and the atomic's
+    // latency hides behind that tile.
+    auto claim = [&]() { if (tid == 0) claimed = n_wg + atomicAdd(a.ws_ctrl, 1); };
 
     // ---- this item
     int kvh, qh_base;
@@ -818,9 +818,7 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
       if (!slot_on) kvh = H - 1;  // keep addresses valid; results are discarded
     }
     float q[XP ? 1 : D / 8];
-    if constexpr (XP) {
-      xqueries(op.q, a.qscale, lane, &x_q[w][0]);  // scores come out in log2 units
-    } else {
+    if constexpr (!XP) {
       int qb;
       bool head_on;
       item_heads<G>(a, it.y, lane, qb, head_on);
@@ -837,8 +835,6 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
     sp.tab = clampi(op.tab, 0, a.pool.num_pages - 1);
 
     float m = -INFINITY, l = 0.0f;
-    const bool has_next = nxt < n_items;
-    auto next_ops = [&]() { if (has_next) item_ops<D, G, XP>(a, nit, lane, nop); };
     int k0 = k_begin + w * TK;
     if constexpr (XP) {
       // accumulators start from a zero made inside the item loop, so the compiler
@@ -850,7 +846,7 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int n = 0; n < 8; ++n) ox[t][n] = v4f{zero, zero, zero, zero};
-      const bf16x8* qsw = &x_q[w][0];
+      const bf16x8* qsw = x_q;
       XBuf xb;
       if (k0 <= k_end) {
         xload(xb, a, sp, k0);
@@ -858,9 +854,9 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
           xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l);
           k0 += STEP;
         }
-        xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l, next_ops);
+        xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l, claim);
       } else {
-        next_ops();
+        claim();
       }
       // ---- l over the lane groups; O = hi rows + mid rows (lanes + 32) + lo rows; to LDS
       l = wave_xor_sum(l, 16);
@@ -898,10 +894,10 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
           decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l);
           k0 += STEP;
         }
-        if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, next_ops);
-        else decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l, next_ops);
+        if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, claim);
+        else decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l, claim);
       } else {
-        next_ops();
+        claim();
       }
       // ---- l per head summed over the slot's key groups; the wave's state to LDS
       l = wave_xor_sum(l, 4);
@@ -915,6 +911,18 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
     }
     if (tid == 0) s_claim[0] = claimed;
     __syncthreads();
+    // the next item's table entries and queries load while this one is combined
+    // (a claim is n_wg + a counter that starts at zero; any other value, from a
+    // workspace whose counter was not zero, ends the workgroup rather than indexing
+    // outside the tables)
+    const int nxt = uni(s_claim[0]);
+    const bool has_next = nxt >= n_wg && nxt < n_items;
+    Item nit = it;
+    ItemOps<XP ? 8 : D / 8> nop;
+    if (has_next) {
+      nit = item_of(a, tabs, nxt, gy);
+      item_ops<D, G, XP>(a, nit, lane, w, nop);
+    }
 
     // ---- combine in wave order: value v = i*4 + r of this lane is head slot*4 + r,
     // d = (lane % 32) * NT + i; wave w finishes the values v with v % NWD == w.
@@ -949,11 +957,11 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
       }
     }
     if (!has_next) break;  // workgroup-uniform
-    const int nn = s_claim[0];
+    // (exact-split path: every wave is past the barrier above, so no tile reads the
+    // query operands any more; the loop-top barrier publishes the new ones)
+    if constexpr (XP) xqueries(nop.q, a.qscale, lane, w, x_q);
     it = nit;
     op = nop;
-    nxt = nn;
-    if (nxt < n_items) nit = item_of(a, tabs, nxt, gy);
   }
 }
 
