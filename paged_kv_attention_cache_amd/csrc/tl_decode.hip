@@ -538,10 +538,13 @@ __device__ __forceinline__ void xqueries(const float (&qraw)[8], float qscale, i
 }
 
 #ifndef TL_DECODE_WAVES
-#define TL_DECODE_WAVES 4
+#define TL_DECODE_WAVES 2
 #endif
-constexpr int NWD = TL_DECODE_WAVES;  // waves per workgroup; they share one split
-constexpr int NTHR = 64 * NWD;
+// Waves per workgroup; they share one split, and the split's combine waits for the
+// slowest of them.  Waves drift apart over a split (their loads are served at
+// different rates), so the register-tile paths use 2 waves on half-size splits; the
+// exact-split path builds its query operands one d step per wave, so it has 4.
+template <bool XP> struct DecodeWaves { static constexpr int value = XP ? 4 : TL_DECODE_WAVES; };
 #ifndef TL_DECODE_MIN_WAVES
 #define TL_DECODE_MIN_WAVES 2
 #endif
@@ -716,7 +719,10 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
 // that workgroup is nearly free: longest-processing-time-first scheduling), and the
 // next item's table entries and queries load while the current item is combined.
 template <int KVT, int D, int G, bool XP>
-__global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::value)) void decode_split_kernel(
+    DecodeArgs a) {
+  constexpr int NWD = DecodeWaves<XP>::value;
+  constexpr int NTHR = 64 * NWD;
   using GE = Geo<KVT, D>;
   constexpr int NT = GE::NT;
   constexpr int PF = DecodePrefetch<KVT, D, G>::value;
@@ -736,7 +742,6 @@ __global__ __launch_bounds__(NTHR, (DecodeOcc<KVT, XP>::value)) void decode_spli
   __shared__ float c_acc[NWD][NT * 4][64];    // [wave][value i*4 + r][lane]
   __shared__ float c_m[NWD][8], c_l[NWD][8];  // [wave][slot*4 + head]
   __shared__ bf16x8 x_q[XP ? 8 * 64 : 1];  // exact-split path: Q3 operands of the item
-  static_assert(!XP || NWD == 4, "each of the 4 waves builds one d step of the exact-split queries");
 
   // ---- numbering tables (inclusive block scans over the batch, NTHR at a time)
   if (tid <= NBKT) c_carry[tid] = 0;
@@ -1029,14 +1034,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int i = 0; i < PER; ++i) dst[i] = l > 0.0f ? o[i] * inv : 0.0f;
 }
 
-// Resident workgroups of one kernel instantiation at a given dynamic LDS size.
-template <typename K>
-int resident_workgroups(K kernel, size_t dyn_lds) {
+// Resident workgroups of one kernel instantiation at a given dynamic LDS size (the
+// cache is per instantiation: each has its own register and LDS footprint).
+template <auto kernel>
+int resident_workgroups(int threads, size_t dyn_lds) {
   static int cached = 0;
   static size_t cached_lds = 0;
   if (cached == 0 || cached_lds != dyn_lds) {
     int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NTHR, dyn_lds) != hipSuccess || per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess || per_cu <= 0)
       per_cu = 1;
 #ifdef TL_DECODE_WG_PER_CU
     per_cu = std::min(per_cu, TL_DECODE_WG_PER_CU);
@@ -1056,8 +1062,9 @@ hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
   const int64_t gy = (G == 8) ? H : (H + 1) / 2;
   const size_t dyn = (size_t)TABLE_INTS * a.batch * sizeof(int);
   const int64_t upper = (int64_t)a.batch * a.n_split * gy;
-  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups(decode_split_kernel<KVT, D, G, XP>, dyn));
-  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP>), dim3((unsigned)wgs), dim3(NTHR), dyn, s, a);
+  constexpr int threads = 64 * DecodeWaves<XP>::value;
+  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups<decode_split_kernel<KVT, D, G, XP>>(threads, dyn));
+  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP>), dim3((unsigned)wgs), dim3(threads), dyn, s, a);
   return hipGetLastError();
 }
 
@@ -1098,7 +1105,7 @@ int decode_split_keys(int kv_dtype, int group, int page_size) {
 #define TL_DECODE_SPLIT_FP8 4096
 #endif
 #ifndef TL_DECODE_SPLIT_OTHER
-#define TL_DECODE_SPLIT_OTHER 1024
+#define TL_DECODE_SPLIT_OTHER 512
 #endif
   const int want = kv_dtype == KV_FP8 ? TL_DECODE_SPLIT_FP8 : TL_DECODE_SPLIT_OTHER;
   return want < 64 * page_size ? want : 64 * page_size;  // a split spans at most 64 pages

@@ -94,9 +94,9 @@ def test_decode_rejects_bad_arguments():
 
 def test_decode_workspace_size_formula():
     p = _pool(dtype=1, page_size=16, head_dim=128)
-    # bf16 splits are 1024 keys (64 pages of 16): 128 blocks of 16 = 2048 keys -> 2 splits
+    # bf16 splits are 512 keys (32 pages of 16): 128 blocks of 16 = 2048 keys -> 4 splits
     n = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p), 3, 8, 128)
-    assert n == 3 * 8 * 2 * (128 + 2) * 4 + 16  # partial states (acc + m, l) and 16 control bytes
+    assert n == 3 * 8 * 4 * (128 + 2) * 4 + 16  # partial states (acc + m, l) and 16 control bytes
     p8 = _pool(dtype=2, page_size=64, head_dim=128)
     n8 = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p8), 2, 16, 512)  # 32768 keys / 4096
     assert n8 == 2 * 16 * 8 * 130 * 4 + 16

@@ -153,7 +153,7 @@ DECODE_CASES = [
     # (name, lens, Hq, Hkv, D, S, dtype, window)
     ("g4_bf16_edges", [1, 2, 31, 32, 33, 100], 8, 2, 128, 16, "bf16", 0),
     ("g8_fp8_split_edges", [511, 2048, 4095, 4096, 4097, 8193, 9000], 16, 2, 128, 64, "fp8", 0),
-    ("g4_bf16_split_edges", [1023, 1024, 1025, 2049, 3000], 8, 2, 128, 16, "bf16", 0),
+    ("g4_bf16_split_edges", [511, 512, 513, 1023, 1024, 1025, 2049, 3000], 8, 2, 128, 16, "bf16", 0),
     ("g8_fp8_page16", [17, 300, 2100], 16, 2, 128, 16, "fp8", 0),
     ("g8_fp8_page8_fallback", [9, 700], 16, 2, 128, 8, "fp8", 0),
     ("g2_f32_d64", [5, 37, 64, 65], 4, 2, 64, 16, "f32", 0),
