@@ -13,4 +13,5 @@ something other than itself (format definitions, closed forms, brute force,
 invariants the pages state, and the pages' printed byte counts).
 """
 from . import encode, paged  # noqa: F401
-from .paged import KVPool, KEY_BLOCK, attend_rows, attend_rows_blockwise, decode, prefill  # noqa: F401
+from .paged import (KVPool, KEY_BLOCK, attend_rows, attend_rows_blockwise, decode, decode_ring,  # noqa: F401
+                    prefill, prefill_ring, ring_slots)

@@ -325,3 +325,105 @@ def attend_history(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
         o = attend_rows(qh, K[:, h], V[:, h], np.repeat(np.asarray(pos), G), window, scale)
         out[:, h * G:(h + 1) * G, :] = o.reshape(R, G, D).astype(np.float32)
     return out
+
+
+# ============================================================= ring (windowed pool)
+# Page "How serving works in Tlaloc", section 3 (windowed KV pool bullets) and
+# section 2 (the ring bullet of PAGED_ATTENTION): a sliding-window layer keeps, per
+# sequence, a ring of R pages.  Logical block b of the sequence lives on the ring's
+# page b % R (the ring table's entry b % R), so position p overwrites position
+# p - R*S.  Attention with ring = true scores the ring's N = R*S slots, masking
+# each by its age: slot i (ring page i // S, offset i % S) holds the position
+# (L - 1 - i) mod N behind the row's last one, and is live when that age is less
+# than the window and less than L.
+#
+# Reading (the pages define the age from "the row's last" position): a decode row
+# has L = seq_len; a prefill token at position p uses its own causal length
+# L = p + 1 (section 1).  A slot is scored with whatever it holds; the pages size
+# calls so that it holds the position its age names (min(p0, W - 1) + n <= N).
+# W <= 0 (no window) leaves only the L bound.  Live slots are gathered oldest
+# first, i.e. in the order of the positions they stand for.
+def ring_slots(ring_row: np.ndarray, positions: np.ndarray, page_size: int) -> np.ndarray:
+    """WINDOW_SLOT_MAPPING: slot of each position on the sequence's ring (-1 for p < 0)."""
+    ring_row = np.asarray(ring_row, dtype=np.int64)
+    R = ring_row.shape[0]
+    p = np.asarray(positions, dtype=np.int64)
+    blk = np.where(p < 0, 0, p) // page_size
+    slot = ring_row[blk % R] * page_size + np.where(p < 0, 0, p) % page_size
+    return np.where(p < 0, -1, slot).astype(np.int32)
+
+
+def ring_live_slots(L: int, window: int, n_slots: int) -> list[int]:
+    """Ring slot indices live for a row of causal length L, oldest first."""
+    live = []
+    for i in range(n_slots):
+        age = (L - 1 - i) % n_slots
+        if age < L and (window <= 0 or age < window):
+            live.append((age, i))
+    live.sort(reverse=True)  # largest age (oldest position) first
+    return [i for _, i in live]
+
+
+def ring_values(pool: KVPool, ring_row: np.ndarray, slots_idx: list[int]):
+    """Stored K and V of the given ring slot indices, widened exactly: [n, H_kv, D] each."""
+    S = pool.page_size
+    ring_row = np.asarray(ring_row, dtype=np.int64)
+    idx = np.asarray(slots_idx, dtype=np.int64)
+    pages = ring_row[idx // S]
+    if idx.size and (pages.min() < 0 or pages.max() >= pool.num_pages):
+        raise ValueError("ring: the ring table names a page outside the pool")
+    off = idx % S
+    k, v = pool.k[pages, :, off, :], pool.v[pages, :, off, :]
+    ks = vs = None
+    if pool.kv_dtype == "fp8":
+        ks, vs = pool.k_scale[pages, :, off], pool.v_scale[pages, :, off]
+    return enc.kv_values(k, ks, pool.kv_dtype), enc.kv_values(v, vs, pool.kv_dtype)
+
+
+def decode_ring(pool: KVPool, q: np.ndarray, ring_tables: np.ndarray, seq_lens: np.ndarray,
+                window: int, scale: float) -> np.ndarray:
+    """PAGED_ATTENTION decode with ring = true.  ring_tables [B, R]: sequence b's ring pages."""
+    q = np.asarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    G = Hq // pool.num_kv_heads
+    N = ring_tables.shape[1] * pool.page_size
+    out = np.zeros((B, Hq, D), dtype=np.float32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        live = ring_live_slots(L, window, N)
+        K, V = ring_values(pool, ring_tables[b], live)
+        n = len(live)
+        for h in range(pool.num_kv_heads):
+            rows = slice(h * G, (h + 1) * G)
+            o = attend_rows(q[b, rows], K[:, h], V[:, h], np.full(G, n - 1), 0, scale)
+            out[b, rows] = o.astype(np.float32)
+    return out
+
+
+def prefill_ring(pool: KVPool, q: np.ndarray, ring_tables: np.ndarray, positions: np.ndarray,
+                 window: int, scale: float) -> np.ndarray:
+    """PAGED_ATTENTION prefill with ring = true: each token masks the ring by its own age.
+
+    q [B, T, H_q, D], positions [B, T] (-1 = pad, output 0).  Returns f32 [B, T, H_q, D].
+    """
+    q = np.asarray(q, dtype=np.float32)
+    positions = np.asarray(positions)
+    B, T, Hq, D = q.shape
+    G = Hq // pool.num_kv_heads
+    N = ring_tables.shape[1] * pool.page_size
+    out = np.zeros((B, T, Hq, D), dtype=np.float32)
+    for b in range(B):
+        for t in range(T):
+            p = int(positions[b, t])
+            if p < 0:
+                continue
+            live = ring_live_slots(p + 1, window, N)
+            K, V = ring_values(pool, ring_tables[b], live)
+            n = len(live)
+            for h in range(pool.num_kv_heads):
+                rows = slice(h * G, (h + 1) * G)
+                o = attend_rows(q[b, t, rows], K[:, h], V[:, h], np.full(G, n - 1), 0, scale)
+                out[b, t, rows] = o.astype(np.float32)
+    return out
