@@ -156,6 +156,42 @@ int tl_paged_attn_prefill(const tl_kv_pool* pool, const float* q, int32_t num_q_
                           size_t workspace_bytes, void* stream);
 
 /*
+ * PAGED_ATTENTION over a windowed pool whose tables are rings ("How serving works in
+ * Tlaloc", section 3, windowed KV pool bullets: each sequence holds a ring of
+ * ring_pages pages and logical block j of the sequence is on ring page j % ring_pages,
+ * so position p overwrites position p - N, N = ring_pages * page_size; section 2, the
+ * ring bullet: with ring = true the ring's N slots are scored, each masked by its
+ * age).  The K/V of position p are written beforehand with tl_kv_cache_write at slot
+ * ring_tables[b][(p / S) % ring_pages] * S + p % S (the windowed slot mapping).
+ *   ring_tables   [batch][ring_pages] int32 page ids of each sequence's ring
+ *   ring_pages    > 0, ring_pages * page_size < 2^30
+ *   window        W > 0: the window; <= 0: none.  A row of causal length L (decode:
+ *                 seq_lens[b]; prefill: position + 1) scores ring slot i when its age
+ *                 (L - 1 - i) mod N is below min(W, L); that is the last min(W, N, L)
+ *                 positions, each read from its ring slot as it stands.  The slot holds
+ *                 the position its age names whenever every call writes at most
+ *                 N - min(p0, W - 1) tokens starting at position p0 (section 3).
+ *   seq_lens, positions: no upper bound (a ring has no end); other arguments, the
+ *                 workspace rules and the results' batch invariance are those of the
+ *                 full-table entries above.
+ * With a ring of at least ceil(W / S) pages (decode) or ceil((W - 1 + n) / S) pages
+ * (prefill calls of n tokens), the results are the same bits as the full-table entry
+ * with window W over a pool holding the same K/V.
+ */
+size_t tl_paged_attn_decode_ring_workspace_size(const tl_kv_pool* pool, int32_t batch,
+                                                int32_t num_q_heads, int32_t ring_pages,
+                                                int32_t window);
+int tl_paged_attn_decode_ring(const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                              const int32_t* ring_tables, int32_t ring_pages,
+                              const int32_t* seq_lens, int32_t batch, int32_t window, float scale,
+                              float* out, void* workspace, size_t workspace_bytes, void* stream);
+int tl_paged_attn_prefill_ring(const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                               const int32_t* ring_tables, int32_t ring_pages,
+                               const int32_t* positions, int32_t batch, int32_t tokens_per_row,
+                               int32_t window, float scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Copy sequence positions 0..length-1 out of the pool in logical order, as stored
  * (no decoding), so that a test can compare written/gathered KV byte for byte
  * ("How serving works in Tlaloc", section 2: the pages a block table names).

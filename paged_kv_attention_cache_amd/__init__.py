@@ -6,7 +6,8 @@ used for device memory and streams.  The binding has no fallback: if the
 library is missing or its call fails, it raises.
 
 Names follow the C ABI: ``tl_kv_cache_write``, ``tl_paged_attn_decode``,
-``tl_paged_attn_prefill``, ``tl_kv_gather`` and the workspace-size queries.
+``tl_paged_attn_prefill``, their ring forms ``tl_paged_attn_decode_ring`` and
+``tl_paged_attn_prefill_ring``, ``tl_kv_gather`` and the workspace-size queries.
 """
 from __future__ import annotations
 
@@ -57,10 +58,15 @@ def lib() -> ctypes.CDLL:
         L.tl_paged_attn_prefill_workspace_size.argtypes = [P, i32, i32, i32, i32]
         L.tl_paged_attn_prefill_workspace_size.restype = sz
         L.tl_paged_attn_prefill.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
+        L.tl_paged_attn_decode_ring_workspace_size.argtypes = [P, i32, i32, i32, i32]
+        L.tl_paged_attn_decode_ring_workspace_size.restype = sz
+        L.tl_paged_attn_decode_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp, sz, vp]
+        L.tl_paged_attn_prefill_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
         L.tl_kv_gather.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
         L.tl_last_error.restype = ctypes.c_char_p
         L.tl_abi_version.restype = ctypes.c_int
-        for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather"):
+        for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather",
+                   "tl_paged_attn_decode_ring", "tl_paged_attn_prefill_ring"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -194,6 +200,60 @@ def tl_paged_attn_prefill(pool: KVPool, q, block_tables, positions, window: int 
                                        positions.data_ptr(), B, T, window, sc, out.data_ptr(), ws_ptr, ws_bytes,
                                        _stream(stream)))
     return out
+
+
+def tl_paged_attn_decode_ring_workspace_size(pool: KVPool, batch: int, num_q_heads: int, ring_pages: int,
+                                             window: int) -> int:
+    ps = pool.c_struct()
+    return int(lib().tl_paged_attn_decode_ring_workspace_size(ctypes.byref(ps), batch, num_q_heads, ring_pages,
+                                                              window))
+
+
+def tl_paged_attn_decode_ring(pool: KVPool, q, ring_tables, seq_lens, window: int = 0, scale: float | None = None,
+                              out=None, workspace=None, stream=None):
+    """PAGED_ATTENTION decode over ring tables: ring_tables int32 [B, ring_pages]."""
+    import torch
+    B, Hq, D = q.shape
+    R = int(ring_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = tl_paged_attn_decode_ring_workspace_size(pool, B, Hq, R, window)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)  # zero before first use
+    ps = pool.c_struct()
+    sc = default_scale(D) if scale is None else scale
+    _check(lib().tl_paged_attn_decode_ring(ctypes.byref(ps), q.data_ptr(), Hq, ring_tables.data_ptr(), R,
+                                           seq_lens.data_ptr(), B, window, sc, out.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tl_paged_attn_prefill_ring(pool: KVPool, q, ring_tables, positions, window: int = 0, scale: float | None = None,
+                               out=None, stream=None):
+    """PAGED_ATTENTION prefill over ring tables: q f32 [B, T, H_q, D]; positions int32 [B, T]."""
+    import torch
+    B, T, Hq, D = q.shape
+    R = int(ring_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    ps = pool.c_struct()
+    sc = default_scale(D) if scale is None else scale
+    _check(lib().tl_paged_attn_prefill_ring(ctypes.byref(ps), q.data_ptr(), Hq, ring_tables.data_ptr(), R,
+                                            positions.data_ptr(), B, T, window, sc, out.data_ptr(), None, 0,
+                                            _stream(stream)))
+    return out
+
+
+def ring_slot_mapping(ring_row, positions, page_size: int):
+    """Windowed slot mapping of a sequence's ring (host helper, numpy): position p is on
+    ring page ring_row[(p // page_size) % len(ring_row)] at offset p % page_size; p < 0
+    gives slot -1."""
+    import numpy as np
+    ring_row = np.asarray(ring_row, dtype=np.int64)
+    p = np.asarray(positions, dtype=np.int64)
+    pc = np.maximum(p, 0)
+    slots = ring_row[(pc // page_size) % len(ring_row)] * page_size + pc % page_size
+    return np.where(p < 0, -1, slots).astype(np.int32)
 
 
 def tl_kv_gather(pool: KVPool, block_table_row, length: int, stream=None):

@@ -121,6 +121,158 @@ int64_t decode_nsplit(const tl_kv_pool* pool, int32_t num_q_heads, int32_t max_b
   return (keys + sk - 1) / sk;
 }
 
+// Keys a ring row can score: the window, at most the ring's N = R * S slots.
+int32_t ring_window(const tl_kv_pool* pool, int32_t ring_pages, int32_t window) {
+  const int64_t n = (int64_t)ring_pages * pool->page_size;
+  return (int32_t)(window > 0 ? std::min<int64_t>(window, n) : n);
+}
+
+// Splits a row of a ring touches: its keys are the last ring_window() positions,
+// which span at most (w - 1) / sk + 2 splits of sk keys.
+int64_t ring_nsplit(const tl_kv_pool* pool, int32_t num_q_heads, int32_t ring_pages, int32_t window) {
+  const int sk = tl::decode_split_keys(pool->dtype, num_q_heads / pool->num_kv_heads, pool->page_size);
+  return (ring_window(pool, ring_pages, window) - 1) / sk + 2;
+}
+
+size_t decode_ws_bytes(const tl_kv_pool* pool, int32_t batch, int32_t num_q_heads, int64_t ns) {
+  // 16 bytes of control words (at offset 0 whatever the shape), then the partial
+  // states (acc, then m and l)
+  return 16 + (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float);
+}
+
+// Shared by the full-table and ring decode entries.  ring = 0: block_tables has
+// max_blocks entries per row, block j at entry j; ring = R: R entries, block j at j % R.
+int decode_common(const char* fn, const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                  const int32_t* block_tables, int32_t max_blocks, int32_t ring, const int32_t* seq_lens,
+                  int32_t batch, int32_t window, float scale, float* out, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if (batch > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: batch (%d) must be <= 65535", fn, batch);
+  if (ring == 0) {
+    if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
+    if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
+      return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
+  } else {
+    if (ring <= 0) return fail(TL_ERR_INVALID, "%s: ring_pages (%d) must be > 0", fn, ring);
+    if ((int64_t)ring * pool->page_size >= ((int64_t)1 << 30))
+      return fail(TL_ERR_UNSUPPORTED, "%s: ring_pages * page_size must be < 2^30", fn);
+  }
+  if (batch == 0) return ok();
+  if (!q) return fail(TL_ERR_INVALID, "%s: q is NULL", fn);
+  if (!out) return fail(TL_ERR_INVALID, "%s: out is NULL", fn);
+  if (!block_tables) return fail(TL_ERR_INVALID, "%s: %s is NULL", fn, ring ? "ring_tables" : "block_tables");
+  if (!seq_lens) return fail(TL_ERR_INVALID, "%s: seq_lens is NULL", fn);
+  if (!aligned(q, 16)) return fail(TL_ERR_INVALID, "%s: q is not 16-byte aligned", fn);
+  if (!aligned(out, 16)) return fail(TL_ERR_INVALID, "%s: out is not 16-byte aligned", fn);
+  if (!aligned(block_tables, 4))
+    return fail(TL_ERR_INVALID, "%s: %s is not 4-byte aligned", fn, ring ? "ring_tables" : "block_tables");
+  if (!aligned(seq_lens, 4)) return fail(TL_ERR_INVALID, "%s: seq_lens is not 4-byte aligned", fn);
+  const int64_t ns = ring ? ring_nsplit(pool, num_q_heads, ring, window) : decode_nsplit(pool, num_q_heads, max_blocks);
+  const size_t need = decode_ws_bytes(pool, batch, num_q_heads, ns);
+  if (!workspace || workspace_bytes < need)
+    return fail(TL_ERR_WORKSPACE, "%s: workspace (%zu bytes) is smaller than the %zu bytes required", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (!aligned(workspace, 16)) return fail(TL_ERR_INVALID, "%s: workspace is not 16-byte aligned", fn);
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t width = ring ? ring : max_blocks;
+  if (validate_mode()) {
+    std::vector<int32_t> lens, tables;
+    if ((rc = copy_to_host(fn, "seq_lens", seq_lens, (size_t)batch, lens, s))) return rc;
+    if ((rc = copy_to_host(fn, "block_tables", block_tables, (size_t)batch * width, tables, s))) return rc;
+    const int64_t n_ring = (int64_t)ring * pool->page_size;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (lens[b] < 0 || (!ring && (int64_t)lens[b] > (int64_t)max_blocks * pool->page_size))
+        return fail(TL_ERR_INVALID, "%s: seq_lens[%d] = %d is outside [0, max_blocks * page_size] (TL_VALIDATE)", fn,
+                    b, lens[b]);
+      const int64_t used = ring ? std::min<int64_t>(lens[b], n_ring) : lens[b];
+      if ((rc = check_tables(fn, pool, tables, width, b, used))) return rc;
+    }
+  }
+  tl::DecodeArgs a;
+  a.pool = pool_args(pool);
+  a.q = q; a.block_tables = block_tables; a.seq_lens = seq_lens; a.out = out;
+  a.ws_ctrl = reinterpret_cast<int*>(workspace);  // same place for every shape
+  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 16);
+  a.ws_ml = a.ws_acc + (size_t)batch * num_q_heads * ns * pool->head_dim;
+  a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = width;
+  a.batch = batch; a.window = ring ? ring_window(pool, ring, window) : window;
+  a.ring = ring;
+  a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->page_size);
+  a.n_split = (int)ns;
+  a.qscale = scale * tl::LOG2E;
+  hipError_t e = tl::launch_decode(a, pool->dtype, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+int prefill_common(const char* fn, const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                   const int32_t* block_tables, int32_t max_blocks, int32_t ring, const int32_t* positions,
+                   int32_t batch, int32_t tokens_per_row, int32_t window, float scale, float* out, void* stream) {
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if (batch > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: batch (%d) must be <= 65535", fn, batch);
+  if (tokens_per_row < 0) return fail(TL_ERR_INVALID, "%s: tokens_per_row (%d) must be >= 0", fn, tokens_per_row);
+  if (ring == 0) {
+    if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
+    if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
+      return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
+  } else {
+    if (ring <= 0) return fail(TL_ERR_INVALID, "%s: ring_pages (%d) must be > 0", fn, ring);
+    if ((int64_t)ring * pool->page_size >= ((int64_t)1 << 30))
+      return fail(TL_ERR_UNSUPPORTED, "%s: ring_pages * page_size must be < 2^30", fn);
+  }
+  if ((int64_t)batch * tokens_per_row * num_q_heads >= ((int64_t)1 << 31) / 128)
+    return fail(TL_ERR_UNSUPPORTED, "%s: batch * tokens_per_row * num_q_heads is too large for one call", fn);
+  if (batch == 0 || tokens_per_row == 0) return ok();
+  if (!q) return fail(TL_ERR_INVALID, "%s: q is NULL", fn);
+  if (!out) return fail(TL_ERR_INVALID, "%s: out is NULL", fn);
+  if (!block_tables) return fail(TL_ERR_INVALID, "%s: %s is NULL", fn, ring ? "ring_tables" : "block_tables");
+  if (!positions) return fail(TL_ERR_INVALID, "%s: positions is NULL", fn);
+  if (!aligned(q, 16)) return fail(TL_ERR_INVALID, "%s: q is not 16-byte aligned", fn);
+  if (!aligned(out, 16)) return fail(TL_ERR_INVALID, "%s: out is not 16-byte aligned", fn);
+  if (!aligned(block_tables, 4))
+    return fail(TL_ERR_INVALID, "%s: %s is not 4-byte aligned", fn, ring ? "ring_tables" : "block_tables");
+  if (!aligned(positions, 4)) return fail(TL_ERR_INVALID, "%s: positions is not 4-byte aligned", fn);
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t width = ring ? ring : max_blocks;
+  if (validate_mode()) {
+    std::vector<int32_t> pos, tables;
+    if ((rc = copy_to_host(fn, "positions", positions, (size_t)batch * tokens_per_row, pos, s))) return rc;
+    if ((rc = copy_to_host(fn, "block_tables", block_tables, (size_t)batch * width, tables, s))) return rc;
+    const int64_t n_ring = (int64_t)ring * pool->page_size;
+    for (int32_t b = 0; b < batch; ++b) {
+      int64_t pmax = -1;
+      for (int32_t t = 0; t < tokens_per_row; ++t) {
+        const int32_t p = pos[(size_t)b * tokens_per_row + t];
+        if (p < -1 || (!ring && (int64_t)p >= (int64_t)max_blocks * pool->page_size))
+          return fail(TL_ERR_INVALID, "%s: positions[%d][%d] = %d is outside [-1, max_blocks * page_size) (TL_VALIDATE)",
+                      fn, b, t, p);
+        pmax = std::max<int64_t>(pmax, p);
+      }
+      const int64_t used = ring ? std::min<int64_t>(pmax + 1, n_ring) : pmax + 1;
+      if ((rc = check_tables(fn, pool, tables, width, b, used))) return rc;
+    }
+  }
+  tl::PrefillArgs a;
+  a.pool = pool_args(pool);
+  a.q = q; a.block_tables = block_tables; a.positions = positions; a.out = out;
+  a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = width;
+  a.batch = batch; a.tokens_per_row = tokens_per_row;
+  a.window = ring ? ring_window(pool, ring, window) : window;
+  a.ring = ring;
+  a.tokens_per_wg = tl::prefill_tokens_per_wg(a.group);
+  a.n_qtiles = (tokens_per_row + a.tokens_per_wg - 1) / a.tokens_per_wg;
+  a.qscale = scale * tl::LOG2E;
+  hipError_t e = tl::launch_prefill(a, pool->dtype, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,65 +326,31 @@ size_t tl_paged_attn_decode_workspace_size(const tl_kv_pool* pool, int32_t batch
   const char* fn = "tl_paged_attn_decode_workspace_size";
   if (check_pool(fn, pool) || check_group(fn, pool, num_q_heads)) return 0;
   if (batch <= 0 || max_blocks <= 0) return 0;
-  const int64_t ns = decode_nsplit(pool, num_q_heads, max_blocks);
-  // 16 bytes of control words (at offset 0 whatever the shape), then the partial
-  // states (acc, then m and l)
-  return 16 + (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float);
+  return decode_ws_bytes(pool, batch, num_q_heads, decode_nsplit(pool, num_q_heads, max_blocks));
 }
 
 int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_heads, const int32_t* block_tables,
                          int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t window, float scale,
                          float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "tl_paged_attn_decode";
-  int rc = check_pool(fn, pool);
-  if (rc) return rc;
-  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
-  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
-  if (batch > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: batch (%d) must be <= 65535", fn, batch);
-  if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
-  if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
-    return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
-  if (batch == 0) return ok();
-  if (!q) return fail(TL_ERR_INVALID, "%s: q is NULL", fn);
-  if (!out) return fail(TL_ERR_INVALID, "%s: out is NULL", fn);
-  if (!block_tables) return fail(TL_ERR_INVALID, "%s: block_tables is NULL", fn);
-  if (!seq_lens) return fail(TL_ERR_INVALID, "%s: seq_lens is NULL", fn);
-  if (!aligned(q, 16)) return fail(TL_ERR_INVALID, "%s: q is not 16-byte aligned", fn);
-  if (!aligned(out, 16)) return fail(TL_ERR_INVALID, "%s: out is not 16-byte aligned", fn);
-  if (!aligned(block_tables, 4)) return fail(TL_ERR_INVALID, "%s: block_tables is not 4-byte aligned", fn);
-  if (!aligned(seq_lens, 4)) return fail(TL_ERR_INVALID, "%s: seq_lens is not 4-byte aligned", fn);
-  const size_t need = tl_paged_attn_decode_workspace_size(pool, batch, num_q_heads, max_blocks);
-  if (!workspace || workspace_bytes < need)
-    return fail(TL_ERR_WORKSPACE, "%s: workspace (%zu bytes) is smaller than the %zu bytes required", fn,
-                workspace ? workspace_bytes : (size_t)0, need);
-  if (!aligned(workspace, 16)) return fail(TL_ERR_INVALID, "%s: workspace is not 16-byte aligned", fn);
-  hipStream_t s = (hipStream_t)stream;
-  if (validate_mode()) {
-    std::vector<int32_t> lens, tables;
-    if ((rc = copy_to_host(fn, "seq_lens", seq_lens, (size_t)batch, lens, s))) return rc;
-    if ((rc = copy_to_host(fn, "block_tables", block_tables, (size_t)batch * max_blocks, tables, s))) return rc;
-    for (int32_t b = 0; b < batch; ++b) {
-      if (lens[b] < 0 || (int64_t)lens[b] > (int64_t)max_blocks * pool->page_size)
-        return fail(TL_ERR_INVALID, "%s: seq_lens[%d] = %d is outside [0, max_blocks * page_size] (TL_VALIDATE)", fn,
-                    b, lens[b]);
-      if ((rc = check_tables(fn, pool, tables, max_blocks, b, lens[b]))) return rc;
-    }
-  }
-  tl::DecodeArgs a;
-  a.pool = pool_args(pool);
-  a.q = q; a.block_tables = block_tables; a.seq_lens = seq_lens; a.out = out;
-  const int64_t ns = decode_nsplit(pool, num_q_heads, max_blocks);
-  a.ws_ctrl = reinterpret_cast<int*>(workspace);  // same place for every shape
-  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 16);
-  a.ws_ml = a.ws_acc + (size_t)batch * num_q_heads * ns * pool->head_dim;
-  a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = max_blocks;
-  a.batch = batch; a.window = window;
-  a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->page_size);
-  a.n_split = (int)ns;
-  a.qscale = scale * tl::LOG2E;
-  hipError_t e = tl::launch_decode(a, pool->dtype, s);
-  if (e != hipSuccess) return hip_fail(fn, e);
-  return ok();
+  return decode_common("tl_paged_attn_decode", pool, q, num_q_heads, block_tables, max_blocks, 0, seq_lens, batch,
+                       window, scale, out, workspace, workspace_bytes, stream);
+}
+
+size_t tl_paged_attn_decode_ring_workspace_size(const tl_kv_pool* pool, int32_t batch, int32_t num_q_heads,
+                                                int32_t ring_pages, int32_t window) {
+  const char* fn = "tl_paged_attn_decode_ring_workspace_size";
+  if (check_pool(fn, pool) || check_group(fn, pool, num_q_heads)) return 0;
+  if (batch <= 0 || ring_pages <= 0 || (int64_t)ring_pages * pool->page_size >= ((int64_t)1 << 30)) return 0;
+  return decode_ws_bytes(pool, batch, num_q_heads, ring_nsplit(pool, num_q_heads, ring_pages, window));
+}
+
+int tl_paged_attn_decode_ring(const tl_kv_pool* pool, const float* q, int32_t num_q_heads, const int32_t* ring_tables,
+                              int32_t ring_pages, const int32_t* seq_lens, int32_t batch, int32_t window, float scale,
+                              float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tl_paged_attn_decode_ring";
+  if (ring_pages <= 0) return fail(TL_ERR_INVALID, "%s: ring_pages (%d) must be > 0", fn, ring_pages);
+  return decode_common(fn, pool, q, num_q_heads, ring_tables, ring_pages, ring_pages, seq_lens, batch, window, scale,
+                       out, workspace, workspace_bytes, stream);
 }
 
 size_t tl_paged_attn_prefill_workspace_size(const tl_kv_pool* pool, int32_t batch, int32_t tokens_per_row,
@@ -245,56 +363,20 @@ int tl_paged_attn_prefill(const tl_kv_pool* pool, const float* q, int32_t num_q_
                           int32_t max_blocks, const int32_t* positions, int32_t batch, int32_t tokens_per_row,
                           int32_t window, float scale, float* out, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  const char* fn = "tl_paged_attn_prefill";
   (void)workspace; (void)workspace_bytes;
-  int rc = check_pool(fn, pool);
-  if (rc) return rc;
-  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
-  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
-  if (batch > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: batch (%d) must be <= 65535", fn, batch);
-  if (tokens_per_row < 0) return fail(TL_ERR_INVALID, "%s: tokens_per_row (%d) must be >= 0", fn, tokens_per_row);
-  if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
-  if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
-    return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
-  if ((int64_t)batch * tokens_per_row * num_q_heads >= ((int64_t)1 << 31) / 128)
-    return fail(TL_ERR_UNSUPPORTED, "%s: batch * tokens_per_row * num_q_heads is too large for one call", fn);
-  if (batch == 0 || tokens_per_row == 0) return ok();
-  if (!q) return fail(TL_ERR_INVALID, "%s: q is NULL", fn);
-  if (!out) return fail(TL_ERR_INVALID, "%s: out is NULL", fn);
-  if (!block_tables) return fail(TL_ERR_INVALID, "%s: block_tables is NULL", fn);
-  if (!positions) return fail(TL_ERR_INVALID, "%s: positions is NULL", fn);
-  if (!aligned(q, 16)) return fail(TL_ERR_INVALID, "%s: q is not 16-byte aligned", fn);
-  if (!aligned(out, 16)) return fail(TL_ERR_INVALID, "%s: out is not 16-byte aligned", fn);
-  if (!aligned(block_tables, 4)) return fail(TL_ERR_INVALID, "%s: block_tables is not 4-byte aligned", fn);
-  if (!aligned(positions, 4)) return fail(TL_ERR_INVALID, "%s: positions is not 4-byte aligned", fn);
-  hipStream_t s = (hipStream_t)stream;
-  if (validate_mode()) {
-    std::vector<int32_t> pos, tables;
-    if ((rc = copy_to_host(fn, "positions", positions, (size_t)batch * tokens_per_row, pos, s))) return rc;
-    if ((rc = copy_to_host(fn, "block_tables", block_tables, (size_t)batch * max_blocks, tables, s))) return rc;
-    for (int32_t b = 0; b < batch; ++b) {
-      int64_t pmax = -1;
-      for (int32_t t = 0; t < tokens_per_row; ++t) {
-        const int32_t p = pos[(size_t)b * tokens_per_row + t];
-        if (p < -1 || (int64_t)p >= (int64_t)max_blocks * pool->page_size)
-          return fail(TL_ERR_INVALID, "%s: positions[%d][%d] = %d is outside [-1, max_blocks * page_size) (TL_VALIDATE)",
-                      fn, b, t, p);
-        pmax = std::max<int64_t>(pmax, p);
-      }
-      if ((rc = check_tables(fn, pool, tables, max_blocks, b, pmax + 1))) return rc;
-    }
-  }
-  tl::PrefillArgs a;
-  a.pool = pool_args(pool);
-  a.q = q; a.block_tables = block_tables; a.positions = positions; a.out = out;
-  a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = max_blocks;
-  a.batch = batch; a.tokens_per_row = tokens_per_row; a.window = window;
-  a.tokens_per_wg = tl::prefill_tokens_per_wg(a.group);
-  a.n_qtiles = (tokens_per_row + a.tokens_per_wg - 1) / a.tokens_per_wg;
-  a.qscale = scale * tl::LOG2E;
-  hipError_t e = tl::launch_prefill(a, pool->dtype, s);
-  if (e != hipSuccess) return hip_fail(fn, e);
-  return ok();
+  return prefill_common("tl_paged_attn_prefill", pool, q, num_q_heads, block_tables, max_blocks, 0, positions, batch,
+                        tokens_per_row, window, scale, out, stream);
+}
+
+int tl_paged_attn_prefill_ring(const tl_kv_pool* pool, const float* q, int32_t num_q_heads, const int32_t* ring_tables,
+                               int32_t ring_pages, const int32_t* positions, int32_t batch, int32_t tokens_per_row,
+                               int32_t window, float scale, float* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const char* fn = "tl_paged_attn_prefill_ring";
+  (void)workspace; (void)workspace_bytes;
+  if (ring_pages <= 0) return fail(TL_ERR_INVALID, "%s: ring_pages (%d) must be > 0", fn, ring_pages);
+  return prefill_common(fn, pool, q, num_q_heads, ring_tables, ring_pages, ring_pages, positions, batch,
+                        tokens_per_row, window, scale, out, stream);
 }
 
 int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t length, void* k_out, void* v_out,

@@ -566,10 +566,11 @@ constexpr int NBKT = 4;
 
 struct SeqSplits { int lo, hi, s_first, s_last, f_first, f_last, nf, p0, p1, np; };  // partial splits p0, p1 (np of them)
 
+template <bool RING>
 __device__ __forceinline__ SeqSplits seq_splits(const DecodeArgs& a, int L) {
   SeqSplits r;
   const int sk = a.split_keys;
-  L = min(L, a.max_blocks * a.pool.page_size);
+  if (!RING) L = min(L, a.max_blocks * a.pool.page_size);  // a ring has no end
   r.np = 0;
   r.p0 = r.p1 = 0;
   if (L <= 0) {
@@ -626,12 +627,15 @@ constexpr int TABLE_INTS = 2 + NBKT;  // ints of LDS per sequence
 // Item number -> (sequence, head group, split).  Workgroup-uniform (made scalar).
 struct Item { int b, y, split; };
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <bool RING>
 __device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTables& t, int it, int gy);
+template <bool RING>
 __device__ __forceinline__ Item item_of(const DecodeArgs& a, const ItemTables& t, int it, int gy) {
-  Item r = item_of_lds(a, t, uni(it), gy);
+  Item r = item_of_lds<RING>(a, t, uni(it), gy);
   r.b = uni(r.b); r.y = uni(r.y); r.split = uni(r.split);
   return r;
 }
+template <bool RING>
 __device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTables& t, int it, int gy) {
   Item r;
   const int n = a.batch;
@@ -640,7 +644,7 @@ __device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTable
   const int n_full = t.full[n - 1];
   if (pair < n_full) {
     r.b = lds_upper(t.full, n, pair);
-    const SeqSplits ss = seq_splits(a, t.len[r.b]);
+    const SeqSplits ss = seq_splits<RING>(a, t.len[r.b]);
     r.split = ss.f_first + (pair - (t.full[r.b] - ss.nf));
     return r;
   }
@@ -651,7 +655,7 @@ __device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTable
     pair -= t.bkt[k][n - 1];
   }
   r.b = lds_upper(t.bkt[k], n, pair);
-  const SeqSplits ss = seq_splits(a, t.len[r.b]);
+  const SeqSplits ss = seq_splits<RING>(a, t.len[r.b]);
   const int before = t.bkt[k][r.b] - (r.b > 0 ? t.bkt[k][r.b - 1] : 0);  // this sequence's count in k
   const int local = pair - (t.bkt[k][r.b] - before);
   // the local-th of this sequence's partial splits that fall in bucket k
@@ -684,11 +688,12 @@ __device__ __forceinline__ void item_heads(const DecodeArgs& a, int y, int lane,
   }
 }
 
-template <int D, int G, bool XP>
+template <int D, int G, bool XP, bool RING>
 __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane, int w,
                                          ItemOps<XP ? 8 : D / 8>& op) {
   const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
-  op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + min(first_block + lane, a.max_blocks - 1)];
+  const int entry = RING ? (first_block + lane) % a.ring : min(first_block + lane, a.max_blocks - 1);
+  op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + entry];
   if constexpr (XP) {
     // lane (c, g) of wave w: head c % 8 of the group, d = 32g + 8w .. +7 (step w)
     const int c = lane & 15, g = lane >> 4;
@@ -718,7 +723,7 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
 // starts its last tile of the current item (so an item goes to a workgroup only when
 // that workgroup is nearly free: longest-processing-time-first scheduling), and the
 // next item's table entries and queries load while the current item is combined.
-template <int KVT, int D, int G, bool XP>
+template <int KVT, int D, int G, bool XP, bool RING>
 __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::value)) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int NWD = DecodeWaves<XP>::value;
@@ -753,7 +758,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     for (int k = 0; k <= NBKT; ++k) cnt[k] = 0;
     if (b < a.batch) {
       const int L = a.seq_lens[b];
-      const SeqSplits ss = seq_splits(a, L);
+      const SeqSplits ss = seq_splits<RING>(a, L);
       cnt[0] = ss.nf;
       const int b0 = ss.np > 0 ? tile_bucket(a, split_tiles(a, ss, ss.p0)) : -1;
       const int b1 = ss.np > 1 ? tile_bucket(a, split_tiles(a, ss, ss.p1)) : -1;
@@ -800,9 +805,9 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   const int n_wg = gridDim.x;
   int cur = blockIdx.x;
   if (cur >= n_items) return;  // workgroup-uniform
-  Item it = item_of(a, tabs, cur, gy);
+  Item it = item_of<RING>(a, tabs, cur, gy);
   ItemOps<XP ? 8 : D / 8> op;
-  item_ops<D, G, XP>(a, it, lane, w, op);
+  item_ops<D, G, XP, RING>(a, it, lane, w, op);
   if constexpr (XP) xqueries(op.q, a.qscale, lane, w, x_q);  // scores come out in log2 units
 
   for (;;) {
@@ -831,7 +836,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
 #pragma unroll
       for (int t = 0; t < D / 8; ++t) q[t] = op.q[t] * qs;
     }
-    const SeqSplits ss = seq_splits(a, uni(tabs.len[it.b]));
+    const SeqSplits ss = seq_splits<RING>(a, uni(tabs.len[it.b]));
     const int k_begin = max(it.split * a.split_keys, ss.lo) & ~(TK - 1);
     const int k_end = min((it.split + 1) * a.split_keys - 1, ss.hi);  // inclusive
     Split sp;
@@ -925,8 +930,8 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     Item nit = it;
     ItemOps<XP ? 8 : D / 8> nop;
     if (has_next) {
-      nit = item_of(a, tabs, nxt, gy);
-      item_ops<D, G, XP>(a, nit, lane, w, nop);
+      nit = item_of<RING>(a, tabs, nxt, gy);
+      item_ops<D, G, XP, RING>(a, nit, lane, w, nop);
     }
 
     // ---- combine in wave order: value v = i*4 + r of this lane is head slot*4 + r,
@@ -954,9 +959,11 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       if (single) {
         a.out[((int64_t)it.b * a.num_q_heads + hq) * D + d] = lsum > 0.0f ? acc * (1.0f / lsum) : 0.0f;
       } else {
-        a.ws_acc[(((int64_t)it.b * a.num_q_heads + hq) * a.n_split + it.split) * D + d] = acc;
+        // a ring row's splits are stored from its first (their numbers grow without end)
+        const int rs = RING ? it.split - ss.s_first : it.split;
+        a.ws_acc[(((int64_t)it.b * a.num_q_heads + hq) * a.n_split + rs) * D + d] = acc;
         if (i == 0 && (lane & 31) == 0) {
-          float* dst = a.ws_ml + (((int64_t)it.b * a.num_q_heads + hq) * a.n_split + it.split) * 2;
+          float* dst = a.ws_ml + (((int64_t)it.b * a.num_q_heads + hq) * a.n_split + rs) * 2;
           *reinterpret_cast<float2*>(dst) = make_float2(ms, lsum);
         }
       }
@@ -983,7 +990,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
   if (bh == 0 && lane == 0) a.ws_ctrl[0] = 0;  // item counter, for the next call
   float* dst = a.out + (int64_t)bh * D + lane * PER;
-  const int L = min(a.seq_lens[b], a.max_blocks * a.pool.page_size);
+  const int L = a.ring > 0 ? a.seq_lens[b] : min(a.seq_lens[b], a.max_blocks * a.pool.page_size);
   if (L <= 0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) dst[i] = 0.0f;
@@ -994,8 +1001,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int s0 = lo / a.split_keys, s1 = hi / a.split_keys;
   if (s0 == s1) return;
   const int ns = s1 - s0 + 1;
-  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (int64_t)bh * a.n_split + s0;
-  const float* acc = a.ws_acc + ((int64_t)bh * a.n_split + s0) * D + lane * PER;
+  const int base = a.ring > 0 ? 0 : s0;  // ring rows store their splits from the first
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (int64_t)bh * a.n_split + base;
+  const float* acc = a.ws_acc + ((int64_t)bh * a.n_split + base) * D + lane * PER;
   float mstar = -INFINITY;
   for (int c = lane; c < ns; c += 64) mstar = fmaxf(mstar, ml[c].x);
 #pragma unroll
@@ -1056,16 +1064,23 @@ int resident_workgroups(int threads, size_t dyn_lds) {
   return cached;
 }
 
-template <int KVT, int D, int G, bool XP>
-hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
+template <int KVT, int D, int G, bool XP, bool RING>
+hipError_t decode_launch_split_r(const DecodeArgs& a, hipStream_t s) {
   const int H = a.pool.num_kv_heads;
   const int64_t gy = (G == 8) ? H : (H + 1) / 2;
   const size_t dyn = (size_t)TABLE_INTS * a.batch * sizeof(int);
   const int64_t upper = (int64_t)a.batch * a.n_split * gy;
   constexpr int threads = 64 * DecodeWaves<XP>::value;
-  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups<decode_split_kernel<KVT, D, G, XP>>(threads, dyn));
-  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP>), dim3((unsigned)wgs), dim3(threads), dyn, s, a);
+  const int64_t wgs = std::min<int64_t>(upper, resident_workgroups<decode_split_kernel<KVT, D, G, XP, RING>>(threads, dyn));
+  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP, RING>), dim3((unsigned)wgs), dim3(threads), dyn, s, a);
   return hipGetLastError();
+}
+
+// ring tables take their own instantiations, so the full-table kernels carry none of
+// the ring's extra live values
+template <int KVT, int D, int G, bool XP>
+hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
+  return a.ring > 0 ? decode_launch_split_r<KVT, D, G, XP, true>(a, s) : decode_launch_split_r<KVT, D, G, XP, false>(a, s);
 }
 
 template <int KVT, int D, int G>

@@ -115,10 +115,11 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* out;
-  float* ws_acc;   // [batch][num_q_heads][n_split][head_dim]
+  float* ws_acc;   // [batch][num_q_heads][n_split][head_dim], split index from the row's first
   float* ws_ml;    // [batch][num_q_heads][n_split][2]
   int* ws_ctrl;    // [4]: the item counter (zero between calls)
   int num_q_heads, group, max_blocks, batch, window, split_keys, n_split;
+  int ring;        // 0: block j of a sequence is block_tables entry j; R > 0: entry j % R
   float qscale;    // scale * log2(e): scores come out in log2 units
 };
 
@@ -129,6 +130,7 @@ struct PrefillArgs {
   const int32_t* positions;
   float* out;
   int num_q_heads, group, max_blocks, batch, tokens_per_row, window, n_qtiles, tokens_per_wg;
+  int ring;        // 0: block j of a sequence is block_tables entry j; R > 0: entry j % R
   float qscale;
 };
 

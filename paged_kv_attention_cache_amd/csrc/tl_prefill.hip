@@ -46,6 +46,9 @@ struct PrefillCfg {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// table entry of a sequence's block: the block itself, or its ring page's entry
+__device__ __forceinline__ int ring_entry(const PrefillArgs& a, int blk) { return a.ring > 0 ? blk % a.ring : blk; }
+
 template <int KVT, int D>
 struct Staged {
   uint4 k[PrefillCfg<KVT, D>::UPT];
@@ -67,7 +70,7 @@ __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs
       {
         const int kk = u % KT, c = u / KT;
         const int key = min(kt0 + kk, key_hi);
-        const int page = clampi(table[key >> sh], 0, a.pool.num_pages - 1);
+        const int page = clampi(table[ring_entry(a, key >> sh)], 0, a.pool.num_pages - 1);
         const uint4* p = reinterpret_cast<const uint4*>(a.pool.k);
         st.k[i] = p[(((int64_t)page * H + h) * C::NC + c) * S + (key & (S - 1))];
         if constexpr (KVT == KV_FP8) st.ks[i] = a.pool.k_scale[((int64_t)page * H + h) * S + (key & (S - 1))];
@@ -76,7 +79,7 @@ __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs
       {
         const int kk = u / C::NC, c = u % C::NC;
         const int key = min(kt0 + kk, key_hi);
-        const int page = clampi(table[key >> sh], 0, a.pool.num_pages - 1);
+        const int page = clampi(table[ring_entry(a, key >> sh)], 0, a.pool.num_pages - 1);
         const uint4* p = reinterpret_cast<const uint4*>(a.pool.v);
         st.v[i] = p[(((int64_t)page * H + h) * S + (key & (S - 1))) * C::NC + c];
         if constexpr (KVT == KV_FP8) st.vs[i] = a.pool.v_scale[((int64_t)page * H + h) * S + (key & (S - 1))];
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillArgs a) {
   const int tok = tile * TPG + w * TPW + col / G;
   const int g = col % G;
   const int hq = h * G + g;
-  const int max_pos = a.max_blocks * a.pool.page_size - 1;
+  const int max_pos = a.ring > 0 ? 0x7FFFFFFF : a.max_blocks * a.pool.page_size - 1;  // a ring has no end
   int pos = -1;
   if (tok < T) pos = min(a.positions[(int64_t)b * T + tok], max_pos);
   const int plo = (pos < 0) ? 0 : (a.window > 0 ? max(0, pos - a.window + 1) : 0);

@@ -132,3 +132,27 @@ def test_last_error_is_cleared_by_a_successful_call():
     assert tl.tl_last_error() != ""
     assert _write(_pool(), n=0) == tl.TL_OK
     assert tl.tl_last_error() == ""
+
+
+def test_ring_entries_reject_bad_arguments_and_size_their_workspace():
+    p = _pool(dtype=1, page_size=16, head_dim=128)
+    L = tl.lib()
+    f = ctypes.c_float(0.1)
+    rc = L.tl_paged_attn_decode_ring(ctypes.byref(p), 0x8000, 8, 0xA000, 0, 0xB000, 2, 64, f, 0xC000, 0x9000, 1 << 30,
+                                     None)
+    assert rc == tl.TL_ERR_INVALID and "ring_pages" in tl.tl_last_error()
+    rc = L.tl_paged_attn_prefill_ring(ctypes.byref(p), 0x8000, 8, 0xA000, -2, 0xB000, 2, 16, 64, f, 0xC000, None, 0,
+                                      None)
+    assert rc == tl.TL_ERR_INVALID and "ring_pages" in tl.tl_last_error()
+    rc = L.tl_paged_attn_decode_ring(ctypes.byref(p), 0x8000, 8, 0, 4, 0xB000, 2, 64, f, 0xC000, 0x9000, 1 << 30, None)
+    assert rc == tl.TL_ERR_INVALID and "ring_tables" in tl.tl_last_error()
+    # ring of 8 pages of 16 = 128 slots; window 100 spans at most 99 // 512 + 2 = 2 splits of 512 keys
+    n = L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 3, 8, 8, 100)
+    assert n == 16 + 3 * 8 * 2 * (128 + 2) * 4
+    # no window: the ring's 128 slots
+    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 3, 8, 8, 0) == n
+    # a window wider than a large ring is cut to the ring: 4096 slots -> 4095 // 512 + 2 = 9 splits
+    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 1, 8, 256, 10 ** 6) == 16 + 8 * 9 * 130 * 4
+    rc = L.tl_paged_attn_decode_ring(ctypes.byref(p), 0x8000, 8, 0xA000, 8, 0xB000, 3, 100, f, 0xC000, 0x9000, n - 1,
+                                     None)
+    assert rc == tl.TL_ERR_WORKSPACE
