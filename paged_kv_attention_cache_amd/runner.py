@@ -7,8 +7,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import KVPool, tl_kv_cache_write, tl_paged_attn_decode, tl_paged_attn_decode_workspace_size, \
-    tl_paged_attn_prefill
+from . import KVPool, tl_kv_cache_write, tl_paged_attn_decode, tl_paged_attn_decode_ring, \
+    tl_paged_attn_decode_ring_workspace_size, tl_paged_attn_decode_workspace_size, tl_paged_attn_prefill
 from .workloads import Workload
 
 SENTINEL = 0xA5
@@ -49,13 +49,19 @@ class DecodeStep:
         self.tables = _t(wl.block_tables, device)
         self.seq_lens = _t(wl.seq_lens, device)
         self.out = torch.empty_like(self.q)
-        nb = tl_paged_attn_decode_workspace_size(pool, wl.batch, wl.num_q_heads, wl.max_blocks)
+        if wl.ring_pages > 0:
+            nb = tl_paged_attn_decode_ring_workspace_size(pool, wl.batch, wl.num_q_heads, wl.ring_pages, wl.window)
+        else:
+            nb = tl_paged_attn_decode_workspace_size(pool, wl.batch, wl.num_q_heads, wl.max_blocks)
         self.workspace = torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)
 
     def write(self, stream=None):
         tl_kv_cache_write(self.pool, self.k_new, self.v_new, self.slots, stream=stream)
 
     def attend(self, stream=None):
+        if self.wl.ring_pages > 0:
+            return tl_paged_attn_decode_ring(self.pool, self.q, self.tables, self.seq_lens, self.wl.window,
+                                             self.wl.scale, out=self.out, workspace=self.workspace, stream=stream)
         return tl_paged_attn_decode(self.pool, self.q, self.tables, self.seq_lens, self.wl.window, self.wl.scale,
                                     out=self.out, workspace=self.workspace, stream=stream)
 

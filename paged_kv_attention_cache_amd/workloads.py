@@ -64,6 +64,7 @@ class Workload:
     spare_pages: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
     history_chunk_tokens: int = 1 << 16
     seed: int = SEED
+    ring_pages: int = 0  # > 0: block_tables are [B, ring_pages] rings (windowed pool)
 
     # ---------------------------------------------------------------- shapes
     @property
@@ -90,6 +91,13 @@ class Workload:
             return max(0, int(self.seq_lens[b]) - 1)
         return int(self.start_pos[b])
 
+    def history_start(self, b: int) -> int:
+        """First history position written: 0, or on a ring the oldest position it still
+        holds once the step token is written (earlier ones would be overwritten)."""
+        if self.ring_pages <= 0:
+            return 0
+        return max(0, self.context_len(b) - self.ring_pages * self.page_size)
+
     # --------------------------------------------------------------- streams
     def _rng(self, tensor_id: int, b: int) -> np.random.Generator:
         return np.random.default_rng([self.seed, self.cfg_id, tensor_id, b])
@@ -108,7 +116,10 @@ class Workload:
         S = self.page_size
         out = np.full(positions.shape, -1, dtype=np.int32)
         live = positions >= 0
-        pages = self.block_tables[b][positions[live] // S].astype(np.int64)
+        blk = positions[live] // S
+        if self.ring_pages > 0:  # windowed pool: block j on the ring's entry j % R
+            blk = blk % self.ring_pages
+        pages = self.block_tables[b][blk].astype(np.int64)
         if np.any(pages < 0):
             raise ValueError(f"sequence {b}: block table has no page for a written position")
         out[live] = (pages * S + positions[live] % S).astype(np.int32)
@@ -135,7 +146,7 @@ class Workload:
                 continue
             k, v = self.seq_kv(b)
             pos = np.arange(h)
-            for a in range(0, h, self.history_chunk_tokens):
+            for a in range(self.history_start(b), h, self.history_chunk_tokens):
                 c = min(h, a + self.history_chunk_tokens)
                 if n + (c - a) > self.history_chunk_tokens and n:
                     yield np.concatenate(ks), np.concatenate(vs), np.concatenate(ss)
@@ -217,6 +228,16 @@ def _assign_pages(wl: Workload, ctx_lens: list[int], num_pages: int | None = Non
     wl.spare_pages = perm[at:]
 
 
+def _assign_rings(wl: Workload, ring_pages: int, spare: int = 0) -> None:
+    """Hand each sequence a ring of ring_pages pages of a seeded permutation, in order."""
+    P = wl.batch * ring_pages + spare
+    perm = np.random.default_rng([wl.seed, wl.cfg_id, T_PERM, 0]).permutation(P).astype(np.int32)
+    wl.num_pages = P
+    wl.ring_pages = ring_pages
+    wl.block_tables = perm[:wl.batch * ring_pages].reshape(wl.batch, ring_pages).copy()
+    wl.spare_pages = perm[wl.batch * ring_pages:]
+
+
 def tiny_decode() -> Workload:
     """Tiny decode step: B=2 at lengths 5 and 37, H_q=4, H_kv=2, D=64, S=16, f32 pool of 8 pages."""
     wl = Workload("c1_tiny_decode", 1, "decode", 2, 4, 2, 64, 16, "f32",
@@ -231,6 +252,17 @@ def llama3_decode(batch: int = 64, lo: int = 512, hi: int = 8192) -> Workload:
     lens = rng.integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
     wl = Workload("c2_llama3_decode_bf16", 2, "decode", batch, 32, 8, 128, 16, "bf16", seq_lens=lens)
     _assign_pages(wl, lens.tolist())
+    return wl
+
+
+def llama3_decode_ring(batch: int = 64, lo: int = 512, hi: int = 8192, window: int = 2048) -> Workload:
+    """The c2 decode layer as a sliding-window layer on a windowed pool: window 2,048,
+    rings of ceil(2048/16) + 1 = 129 pages (section 3's default of one spare page)."""
+    rng = np.random.default_rng([SEED, 2, T_LENGTHS, 0])  # the same lengths as c2
+    lens = rng.integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+    wl = Workload("c2r_llama3_decode_bf16_window2048_ring", 6, "decode", batch, 32, 8, 128, 16, "bf16",
+                  window=window, seq_lens=lens)
+    _assign_rings(wl, -(-window // 16) + 1)
     return wl
 
 
@@ -271,6 +303,7 @@ CONFIGS = {
     "c4": long_prefill,
     "c4w": lambda: long_prefill(window=4096),
     "c5": fp8_decode,
+    "c2r": llama3_decode_ring,
 }
 
 

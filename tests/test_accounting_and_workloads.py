@@ -132,3 +132,29 @@ def test_history_batches_chunking_covers_every_history_token_once():
     for b in range(3):
         want += wl.slots_for(b, np.arange(int(wl.seq_lens[b]) - 1)).tolist()
     assert sorted(seen) == sorted(want)
+
+
+def test_ring_workload_writes_what_the_ring_holds_once():
+    """c2r: each sequence's ring of 129 pages receives its last 129*16 positions (the
+    history's tail, then the step token), each ring slot once, at the windowed slot
+    mapping (block j on ring entry j % 129)."""
+    wl = W.make("c2r")
+    R, S = wl.ring_pages, wl.page_size
+    assert R == 129 and wl.window == 2048 and wl.block_tables.shape == (wl.batch, R)
+    assert len(np.unique(wl.block_tables)) == wl.batch * R  # rings do not share pages
+    seen = {}
+    for k, v, s in wl.history_batches():
+        assert len(np.unique(s)) == len(s)
+        for x in s.tolist():
+            seen[x] = seen.get(x, 0) + 1
+    ks, vs, ss = wl.decode_step_rows()
+    for x in ss.tolist():
+        seen[x] = seen.get(x, 0) + 1
+    assert max(seen.values()) == 1
+    for b in (0, 7, wl.batch - 1):
+        L = int(wl.seq_lens[b])
+        p = np.arange(max(0, L - R * S), L)
+        want = wl.block_tables[b][(p // S) % R] * S + p % S
+        assert np.array_equal(wl.slots_for(b, p), want)
+        assert all(int(x) in seen for x in want)
+    assert len(seen) == sum(min(int(L), R * S) for L in wl.seq_lens)
