@@ -1,4 +1,5 @@
-"""KV storage encoders of the oracle: f32 copy, bf16, fp8 e4m3fn with a per-row scale.
+"""KV storage encoders of the oracle: f32 copy, bf16, fp8 e4m3fn with a per-row scale,
+and the pages' own unscaled fp8 e4m3fn.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module;
 only tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
@@ -11,6 +12,9 @@ Sources (page "How serving works in Tlaloc"):
   codes rounded to nearest even;
 - section 6 "Int8 weights", FP8 KV cache paragraph: values clamped to +-448
   before the convert (e4m3fn has no infinity; 448 is its largest finite value).
+  That paragraph's pool has no scale at all: a value is stored as itself, so one
+  beyond +-448 saturates ("fp8u" below); the scaled form ("fp8") is the
+  per-(token, head) scale of the fp8 decode workload.
 - section 6 "Int8 weights", the int8 formula: a scale of 1 for an all-zero row.
 
 Everything here is written from the format definitions, not from a library
@@ -119,6 +123,14 @@ def fp8_quantize_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return fp8_code(y), scale
 
 
+def fp8_unscaled(x: np.ndarray) -> np.ndarray:
+    """The pages' fp8 KV: code = RNE_e4m3fn(clamp(x, -448, 448)), no scale."""
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("fp8_unscaled: non-finite input")
+    return fp8_code(np.clip(x, np.float32(-FP8_MAX), np.float32(FP8_MAX)))
+
+
 # ------------------------------------------------------------- KV dtypes
 def encode_kv(x: np.ndarray, kv_dtype: str) -> tuple[np.ndarray, np.ndarray | None]:
     """Encode f32 rows [..., D] for storage: (raw, scale or None)."""
@@ -129,6 +141,8 @@ def encode_kv(x: np.ndarray, kv_dtype: str) -> tuple[np.ndarray, np.ndarray | No
         return bf16_bits(x), None
     if kv_dtype == "fp8":
         return fp8_quantize_rows(x)
+    if kv_dtype == "fp8u":
+        return fp8_unscaled(x), None
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
@@ -140,7 +154,9 @@ def kv_values(raw: np.ndarray, scale: np.ndarray | None, kv_dtype: str) -> np.nd
         return bf16_value(raw)
     if kv_dtype == "fp8":
         return fp8_value(raw) * np.asarray(scale, dtype=np.float64)[..., None]
+    if kv_dtype == "fp8u":
+        return fp8_value(raw)
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
-RAW_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+RAW_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8u": np.uint8}

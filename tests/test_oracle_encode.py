@@ -187,3 +187,26 @@ def test_fp8_rows_quarter_of_f32_bytes():
     codes, _ = E.fp8_quantize_rows(x)
     assert codes.nbytes / x.nbytes == g["fp8_pool_quarter"]["ratio"]
     assert E.fp8_value(np.array([0x7E]))[0] == g["fp8_scale_rule"]["max_code_value"]
+
+
+def test_fp8_unscaled_is_the_nearest_code_of_the_clamped_value():
+    """Page section 6, FP8 KV cache paragraph: no scale, values clamped to +-448 and
+    converted; checked by brute-force nearest search over the 254 finite codes (ties
+    to the even code), including values far beyond 448 and below the smallest
+    subnormal."""
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(20000) * rng.choice([1e-3, 1.0, 30.0, 1e3], 20000),
+                        [448.0, 449.0, 464.0, 1e6, -1e6, 2.0 ** -10, -(2.0 ** -10), 0.0, -0.0]]).astype(np.float32)
+    codes = E.fp8_unscaled(x)
+    table = E.fp8_value(np.arange(256, dtype=np.uint8))
+    finite = np.nonzero(np.isfinite(table))[0]
+    for xi, ci in zip(x[:3000].tolist() + x[-9:].tolist(), codes[:3000].tolist() + codes[-9:].tolist()):
+        y = min(max(xi, -448.0), 448.0)
+        d = np.abs(table[finite] - y)
+        best = finite[d == d.min()]
+        if len(best) > 1:  # a tie: the even code (mantissa lsb 0), sign from y
+            best = [b for b in best if (b & 1) == 0 and (b >> 7) == (1 if np.signbit(y) else 0)] or best
+        assert E.fp8_value(np.array([ci], np.uint8))[0] == table[best[0]], (xi, ci, best)
+    assert codes[-6] == 0x7E and codes[-5] == 0xFE  # 1e6 and -1e6 saturate to +-448
+    raw, sc = E.encode_kv(x.reshape(-1, 1), "fp8u")
+    assert sc is None and np.array_equal(E.kv_values(raw, None, "fp8u").reshape(-1), E.fp8_value(codes))
