@@ -20,8 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # TL_LIBRARY may point at another build of the same ABI (e.g. a tuning variant)
 LIB_PATH = os.environ.get("TL_LIBRARY") or os.path.join(HERE, "libtl.so")
 
-KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8u": 3}  # fp8: per-(token, head) scales; fp8u: none
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1}
 
 TL_OK, TL_ERR_INVALID, TL_ERR_UNSUPPORTED, TL_ERR_WORKSPACE, TL_ERR_HIP = 0, -1, -2, -3, -4
 
@@ -113,7 +113,7 @@ class KVPool:
                  device="cuda", fill_byte: int | None = None) -> "KVPool":
         import torch
         x = 16 // ELEM_BYTES[kv_dtype]
-        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[kv_dtype]
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "fp8u": torch.uint8}[kv_dtype]
         kshape = (num_pages, num_kv_heads, head_dim // x, page_size, x)
         vshape = (num_pages, num_kv_heads, page_size, head_dim)
         mk = (lambda s, dt: torch.empty(s, dtype=dt, device=device))

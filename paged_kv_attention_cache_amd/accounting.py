@@ -19,7 +19,7 @@ import math
 
 import numpy as np
 
-BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1}  # fp8u: the unscaled fp8 pool
 
 
 # ----------------------------------------------------- page-level formulas

@@ -65,7 +65,7 @@ __device__ __forceinline__ int page_uniform(int tab, int local) { return __built
 // this tile computes.  Chosen by what fits in the register budget (fp8 tiles are
 // small; bf16 and f32 tiles at D = 128 rely on more waves per SIMD instead).
 template <int KVT, int D, int G> struct DecodePrefetch {
-  static constexpr int value = (KVT == KV_FP8 && D == 128 && G == 8) ? 1 : (D == 64 ? 1 : 0);
+  static constexpr int value = (kv_fp8(KVT) && D == 128 && G == 8) ? 1 : (D == 64 ? 1 : 0);
 };
 
 struct Split {
@@ -85,7 +85,7 @@ __device__ __forceinline__ void load_k(KBuf<KVT, D>& t, const DecodeArgs& a, con
                       (key & (S - 1));
 #pragma unroll
   for (int c = 0; c < GE::NC; ++c) t.k[c] = stream_load(base + (int64_t)c * S);
-  if constexpr (KVT == KV_FP8) {
+  if constexpr (kv_scaled(KVT)) {
     const int g0 = clampi(k0 + kg * 4, sp.lo & ~3, sp.hi & ~3);
     const int pg = page_of_lane(sp.tab, clampi((g0 >> sh) - sp.first_block, 0, 63));
     const int64_t idx = ((int64_t)pg * H + sp.kvh) * S + (g0 & (S - 1));
@@ -259,7 +259,7 @@ __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp
     const int key = k0 + kg * 4 + r;
     const bool valid = key >= sp.lo && key <= sp.k_end;
     float x = sc[r];
-    if constexpr (KVT == KV_FP8) x *= kc.ks[r];
+    if constexpr (kv_scaled(KVT)) x *= kc.ks[r];
     s[r] = valid ? x : -INFINITY;
     tmax = fmaxf(tmax, s[r]);
   }
@@ -280,7 +280,7 @@ __device__ __forceinline__ void decode_tile(const DecodeArgs& a, const Split& sp
   float pv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if constexpr (KVT == KV_FP8) pv[r] = (s[r] == -INFINITY) ? 0.0f : p[r] * kc.vs[r];
+    if constexpr (kv_scaled(KVT)) pv[r] = (s[r] == -INFINITY) ? 0.0f : p[r] * kc.vs[r];
     else pv[r] = p[r];
   }
   // rescale the value accumulators: register r of a quad holds head r of the slot
@@ -404,10 +404,13 @@ __device__ __forceinline__ void xload_v(XBuf& t, const DecodeArgs& a, const Spli
     }
   }
 }
+template <bool SC>
 __device__ __forceinline__ void xload(XBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
   xload_k(t, a, sp, k0);
-  xload_scales(t, a, sp, k0, true);
-  xload_scales(t, a, sp, k0, false);
+  if constexpr (SC) {
+    xload_scales(t, a, sp, k0, true);
+    xload_scales(t, a, sp, k0, false);
+  }
   xload_v(t, a, sp, k0);
 }
 
@@ -416,7 +419,7 @@ __device__ __forceinline__ void xload(XBuf& t, const DecodeArgs& a, const Split&
 // ([col tile][d step][lane]); o: [row tile][d tile].  The running max m only moves
 // when a tile's max exceeds it by more than 8 (log2 units, a factor 2^8), so the
 // accumulators are rarely rescaled; probabilities then stay below 2^8.
-template <typename Hook = NoHook>
+template <bool SC, typename Hook = NoHook>
 __device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf& t, int k0, int k_next,
                                       const bf16x8* qs, v4f (&o)[2][8], float& m, float& l, Hook hook = Hook()) {
   const int c = sp.lane & 15, g = sp.lane >> 4;
@@ -450,10 +453,10 @@ __device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf
     const int h = e >> 2, r = e & 3;
     const int key = k0 + 16 * h + 4 * g + r;
     const bool valid = key >= sp.lo && key <= sp.k_end;
-    s8[e] = valid ? sc[h][r] * t.ks[h][r] : -INFINITY;
+    s8[e] = valid ? (SC ? sc[h][r] * t.ks[h][r] : sc[h][r]) : -INFINITY;
     tmax = fmaxf(tmax, s8[e]);
   }
-  if (more) xload_scales(t, a, sp, k_next, true);
+  if (SC && more) xload_scales(t, a, sp, k_next, true);
   tmax = wave_xor_max(tmax, 16);
   tmax = wave_xor_max(tmax, 32);
   // lazy max: keep m unless this tile exceeds it by more than 8 (or m is unset)
@@ -466,10 +469,10 @@ __device__ __forceinline__ void xtile(const DecodeArgs& a, const Split& sp, XBuf
   for (int e = 0; e < 8; ++e) {
     const float p = fast_exp2(s8[e] - m_use);
     psum += p;
-    const float pv = (s8[e] == -INFINITY) ? 0.0f : p * t.vs[e >> 2][e & 3];
+    const float pv = (s8[e] == -INFINITY) ? 0.0f : (SC ? p * t.vs[e >> 2][e & 3] : p);
     split3(pv, ph[e], pm[e], pl[e]);
   }
-  if (more) xload_scales(t, a, sp, k_next, false);
+  if (SC && more) xload_scales(t, a, sp, k_next, false);
   l = l * alpha + psum;
   m = m_new;
   // ---- A operands of the value product: rows hi / mid (tile 0) and lo (tile 1)
@@ -859,12 +862,13 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       const bf16x8* qsw = x_q;
       XBuf xb;
       if (k0 <= k_end) {
-        xload(xb, a, sp, k0);
+        constexpr bool SC = kv_scaled(KVT);
+        xload<SC>(xb, a, sp, k0);
         while (k0 + STEP <= k_end) {
-          xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l);
+          xtile<SC>(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l);
           k0 += STEP;
         }
-        xtile(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l, claim);
+        xtile<SC>(a, sp, xb, k0, k0 + STEP, qsw, ox, m, l, claim);
       } else {
         claim();
       }
@@ -1086,7 +1090,7 @@ hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
 template <int KVT, int D, int G>
 hipError_t decode_launch_split(const DecodeArgs& a, hipStream_t s) {
   // the exact bf16-split tile serves fp8 pools at D = 128, G = 8 with pages of >= 16
-  if constexpr (KVT == KV_FP8 && D == 128 && G == 8) {
+  if constexpr (kv_fp8(KVT) && D == 128 && G == 8) {
     if (a.pool.page_size >= 16) return decode_launch_split_x<KVT, D, G, true>(a, s);
   }
   return decode_launch_split_x<KVT, D, G, false>(a, s);
@@ -1122,7 +1126,7 @@ int decode_split_keys(int kv_dtype, int group, int page_size) {
 #ifndef TL_DECODE_SPLIT_OTHER
 #define TL_DECODE_SPLIT_OTHER 512
 #endif
-  const int want = kv_dtype == KV_FP8 ? TL_DECODE_SPLIT_FP8 : TL_DECODE_SPLIT_OTHER;
+  const int want = kv_fp8(kv_dtype) ? TL_DECODE_SPLIT_FP8 : TL_DECODE_SPLIT_OTHER;
   return want < 64 * page_size ? want : 64 * page_size;  // a split spans at most 64 pages
 }
 
@@ -1143,7 +1147,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s) {
     switch (kv_dtype) {
       case KV_F32: e = decode_dispatch<KV_F32>(c, s); break;
       case KV_BF16: e = decode_dispatch<KV_BF16>(c, s); break;
-      default: e = decode_dispatch<KV_FP8>(c, s); break;
+      case KV_FP8: e = decode_dispatch<KV_FP8>(c, s); break;
+      default: e = decode_dispatch<KV_FP8U>(c, s); break;
     }
     if (e != hipSuccess) return e;
   }

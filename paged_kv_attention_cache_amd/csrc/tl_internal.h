@@ -13,12 +13,15 @@ namespace tl {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP8U = 3 };
+constexpr bool kv_fp8(int k) { return k == KV_FP8 || k == KV_FP8U; }  // e4m3fn codes
+constexpr bool kv_scaled(int k) { return k == KV_FP8; }               // with (token, head) scales
 
 template <int KVT> struct KvTraits;
 template <> struct KvTraits<KV_F32> { typedef float T; static constexpr int BYTES = 4; static constexpr int X = 4; };
 template <> struct KvTraits<KV_BF16> { typedef uint16_t T; static constexpr int BYTES = 2; static constexpr int X = 8; };
 template <> struct KvTraits<KV_FP8> { typedef uint8_t T; static constexpr int BYTES = 1; static constexpr int X = 16; };
+template <> struct KvTraits<KV_FP8U> : KvTraits<KV_FP8> {};
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int KEY_BLOCK = 2048;  // the pages' key-block width; loop bounds are taken per block

@@ -73,7 +73,7 @@ __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs
         const int page = clampi(table[ring_entry(a, key >> sh)], 0, a.pool.num_pages - 1);
         const uint4* p = reinterpret_cast<const uint4*>(a.pool.k);
         st.k[i] = p[(((int64_t)page * H + h) * C::NC + c) * S + (key & (S - 1))];
-        if constexpr (KVT == KV_FP8) st.ks[i] = a.pool.k_scale[((int64_t)page * H + h) * S + (key & (S - 1))];
+        if constexpr (kv_scaled(KVT)) st.ks[i] = a.pool.k_scale[((int64_t)page * H + h) * S + (key & (S - 1))];
       }
       // V unit u: key u / NC, part u % NC (row-major V)
       {
@@ -82,7 +82,7 @@ __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs
         const int page = clampi(table[ring_entry(a, key >> sh)], 0, a.pool.num_pages - 1);
         const uint4* p = reinterpret_cast<const uint4*>(a.pool.v);
         st.v[i] = p[(((int64_t)page * H + h) * S + (key & (S - 1))) * C::NC + c];
-        if constexpr (KVT == KV_FP8) st.vs[i] = a.pool.v_scale[((int64_t)page * H + h) * S + (key & (S - 1))];
+        if constexpr (kv_scaled(KVT)) st.vs[i] = a.pool.v_scale[((int64_t)page * H + h) * S + (key & (S - 1))];
       }
     }
   }
@@ -100,7 +100,7 @@ __device__ __forceinline__ void stage_store(const Staged<KVT, D>& st, float* kl,
       {
         const int kk = u % KT, c = u / KT;
         widen_chunk<KVT>(st.k[i], x);
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (kv_scaled(KVT)) {
 #pragma unroll
           for (int e = 0; e < X; ++e) x[e] *= st.ks[i];
         }
@@ -111,7 +111,7 @@ __device__ __forceinline__ void stage_store(const Staged<KVT, D>& st, float* kl,
       {
         const int kk = u / C::NC, c = u % C::NC;
         widen_chunk<KVT>(st.v[i], x);
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (kv_scaled(KVT)) {
 #pragma unroll
           for (int e = 0; e < X; ++e) x[e] *= st.vs[i];
         }
@@ -296,7 +296,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t s) {
   switch (kv_dtype) {
     case KV_F32: return prefill_dispatch<KV_F32>(a, s);
     case KV_BF16: return prefill_dispatch<KV_BF16>(a, s);
-    default: return prefill_dispatch<KV_FP8>(a, s);
+    case KV_FP8: return prefill_dispatch<KV_FP8>(a, s);
+    default: return prefill_dispatch<KV_FP8U>(a, s);
   }
 }
 

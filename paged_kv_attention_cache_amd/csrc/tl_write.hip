@@ -44,6 +44,16 @@ __device__ __forceinline__ void encode_row(const float (&x)[D / ROW_LANES], type
   } else if constexpr (KVT == KV_BF16) {
 #pragma unroll
     for (int i = 0; i < E; ++i) enc[i] = (uint16_t)f32_to_bf16(x[i]);
+  } else if constexpr (KVT == KV_FP8U) {
+    // no scale: the value itself, saturated at +-448, to the nearest code
+#pragma unroll
+    for (int i = 0; i < E; i += 2) {
+      const float y0 = fminf(fmaxf(x[i], -448.0f), 448.0f);
+      const float y1 = fminf(fmaxf(x[i + 1], -448.0f), 448.0f);
+      const int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      enc[i] = (uint8_t)(w & 0xFF);
+      enc[i + 1] = (uint8_t)((w >> 8) & 0xFF);
+    }
   } else {
     float m = 0.0f;
 #pragma unroll
@@ -97,7 +107,7 @@ __global__ __launch_bounds__(WG) void write_kernel(WriteArgs a) {
   // instruction of the 8 lanes covers one contiguous span of the destination.
   constexpr int UE = (X * ROW_LANES <= D) ? X : D / ROW_LANES;
   constexpr int NU = E / UE;  // units per lane
-  constexpr bool NTL = KVT != KV_FP8, NTS = KVT == KV_FP8;
+  constexpr bool NTL = !kv_fp8(KVT), NTS = kv_fp8(KVT);
   float xk[E], xv[E];
   {
     const u4* sk = reinterpret_cast<const u4*>(a.k_new + row * D);
@@ -140,7 +150,7 @@ __global__ __launch_bounds__(WG) void write_kernel(WriteArgs a) {
       }
     }
   }
-  if constexpr (KVT == KV_FP8) {
+  if constexpr (kv_scaled(KVT)) {
     if (lane_in_row == 0) {
       const int64_t si = ((int64_t)page * H + h) * S + off;
       a.k_scale[si] = sck;
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(WG) void gather_kernel(GatherArgs a) {
     reinterpret_cast<uint4*>(a.k_out)[u] = kv;
     reinterpret_cast<uint4*>(a.v_out)[u] = vv;
   }
-  if constexpr (KVT == KV_FP8) {
+  if constexpr (kv_scaled(KVT)) {
     const int64_t n = (int64_t)a.length * H;
     if (u < n) {
       const int h = (int)(u % H);
@@ -213,7 +223,8 @@ hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s) {
   switch (kv_dtype) {
     case KV_F32: return write_dispatch<KV_F32>(a, s);
     case KV_BF16: return write_dispatch<KV_BF16>(a, s);
-    default: return write_dispatch<KV_FP8>(a, s);
+    case KV_FP8: return write_dispatch<KV_FP8>(a, s);
+    default: return write_dispatch<KV_FP8U>(a, s);
   }
 }
 
@@ -222,7 +233,8 @@ hipError_t launch_gather(const GatherArgs& a, int kv_dtype, hipStream_t s) {
   switch (kv_dtype) {
     case KV_F32: return gather_dispatch<KV_F32>(a, s);
     case KV_BF16: return gather_dispatch<KV_BF16>(a, s);
-    default: return gather_dispatch<KV_FP8>(a, s);
+    case KV_FP8: return gather_dispatch<KV_FP8>(a, s);
+    default: return gather_dispatch<KV_FP8U>(a, s);
   }
 }
 

@@ -53,7 +53,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    kv_dtype: str  # "f32" | "bf16" | "fp8"
+    kv_dtype: str  # "f32" | "bf16" | "fp8" (scaled) | "fp8u" (unscaled)
     window: int = 0  # <= 0: full attention
     seq_lens: np.ndarray | None = None  # decode: [B] int32, incl. the new token
     tokens_per_row: int = 0  # prefill: T
@@ -296,6 +296,16 @@ def fp8_decode(batch: int = 128, lo: int = 1024, hi: int = 32768) -> Workload:
     return wl
 
 
+def fp8_unscaled_decode(batch: int = 128, lo: int = 1024, hi: int = 32768) -> Workload:
+    """c5's lengths and shape on the pages' own unscaled fp8 pool (no scale arrays)."""
+    rng = np.random.default_rng([SEED, 5, T_LENGTHS, 0])  # the same lengths as c5
+    u = rng.uniform(math.log(lo), math.log(hi), size=batch)
+    lens = np.clip(np.round(np.exp(u)), lo, hi).astype(np.int32)
+    wl = Workload("c5u_fp8_unscaled_decode", 7, "decode", batch, 64, 8, 128, 64, "fp8u", seq_lens=lens)
+    _assign_pages(wl, lens.tolist())
+    return wl
+
+
 CONFIGS = {
     "c1": tiny_decode,
     "c2": llama3_decode,
@@ -304,6 +314,7 @@ CONFIGS = {
     "c4w": lambda: long_prefill(window=4096),
     "c5": fp8_decode,
     "c2r": llama3_decode_ring,
+    "c5u": fp8_unscaled_decode,
 }
 
 

@@ -18,7 +18,9 @@ from tests.helpers import row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 2e-5, "bf16": 2e-5, "fp8": 1e-2}
+# fp8u (the unscaled fp8 pool) stores values that widen exactly, so its outputs are
+# held to the f32 bound; scaled fp8 is compared with the dequantised oracle at 1e-2.
+TOL = {"f32": 2e-5, "bf16": 2e-5, "fp8": 1e-2, "fp8u": 2e-5}
 
 
 @pytest.fixture(scope="module")
@@ -51,7 +53,7 @@ def assert_pool_equal(gpu_pool, opool):
 
 
 # ====================================================================== writes
-@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_write_bit_exact_with_sentinels(torch_cuda, kv_dtype, D):
     torch = torch_cuda
@@ -127,7 +129,7 @@ def test_bf16_write_matches_oracle_on_tie_strata(torch_cuda):
     assert np.array_equal(vv.reshape(P * S, D)[:n], want)
 
 
-@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u"])
 def test_gather_bit_exact(torch_cuda, kv_dtype):
     torch = torch_cuda
     import paged_kv_attention_cache_amd as tl
@@ -164,6 +166,9 @@ DECODE_CASES = [
     ("g8_bf16_odd_heads", [77, 1200], 24, 3, 128, 16, "bf16", 0),
     ("g4_fp8_d64", [129, 1030], 12, 3, 64, 16, "fp8", 0),
     ("zero_length", [0, 5, 0, 1], 8, 2, 128, 16, "bf16", 0),
+    ("g8_fp8u_exact_split", [1, 300, 4095, 4097, 9000], 16, 2, 128, 64, "fp8u", 0),
+    ("g4_fp8u_window", [3000, 700, 5], 8, 2, 128, 16, "fp8u", 900),
+    ("g2_fp8u_d64_page8", [9, 700], 4, 2, 64, 8, "fp8u", 0),
 ]
 
 
@@ -260,6 +265,7 @@ PREFILL_CASES = [
     ("window_crosses_block", [100], [2030], 100, 8, 2, 128, 16, "bf16", 60),
     ("window_longer_than_context", [30], [5], 32, 8, 2, 128, 16, "bf16", 5000),
     ("g4_d64_window1", [20], [3], 20, 8, 2, 64, 8, "bf16", 1),
+    ("g8_fp8u_history", [45, 3], [70, 0], 48, 16, 2, 128, 16, "fp8u", 0),
 ]
 
 
@@ -371,3 +377,31 @@ def test_full_prefill_config_sampled(torch_cuda, cfg):
         err = row_rel_err(out[b, ts], ref)
         assert err <= TOL[wl.kv_dtype], f"{cfg} row {b}: {err:.3e}"
     assert np.all(np.isfinite(out))
+
+
+def test_fp8u_write_saturates_and_rounds_like_the_oracle(torch_cuda):
+    """The unscaled fp8 pool: values beyond +-448 saturate, the rest go to the nearest
+    code (ties even), with no scale stored; every e4m3fn midpoint and its neighbours."""
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    pos = E.FP8_E4M3FN[:0x7F]
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    vals = np.concatenate([pos.astype(np.float32), mid, np.nextafter(mid, np.float32(np.inf)),
+                           np.nextafter(mid, np.float32(-np.inf)),
+                           np.array([448.0, 449.0, 464.0, 1e6, 3e38], np.float32)])
+    vals = np.concatenate([vals, -vals])
+    D, H, S = 128, 1, 16
+    n = (len(vals) + D - 1) // D
+    x = np.zeros(n * D, np.float32)
+    x[:len(vals)] = vals
+    k = x.reshape(n, H, D)
+    P = (n + S - 1) // S
+    gp = tl.KVPool.allocate(P, S, H, D, "fp8u", fill_byte=0)
+    kt = torch.from_numpy(k).cuda()
+    tl.tl_kv_cache_write(gp, kt, kt, torch.arange(n, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    kk, vv, ks, _ = R.pool_logical(gp)
+    assert ks is None
+    want = E.fp8_unscaled(k.reshape(n, D))
+    assert np.array_equal(kk.reshape(P * S, D)[:n], want)
+    assert np.array_equal(vv.reshape(P * S, D)[:n], want)
