@@ -15,6 +15,11 @@ Sources (page "How serving works in Tlaloc"):
   That paragraph's pool has no scale at all: a value is stored as itself, so one
   beyond +-448 saturates ("fp8u" below); the scaled form ("fp8") is the
   per-(token, head) scale of the fp8 decode workload.
+- section 6 "Int8 weights", the int8 formula (scale = max|W| / 127 per output row, 1
+  for an all-zero row; code = clamp(round_half_even(W / scale), -127, 127)).  The
+  pages list int8 KV pools as not built; the reading here applies that formula to
+  each stored (token, kv head) row ("int8" below), as the scaled fp8 pool does with
+  448.
 - section 6 "Int8 weights", the int8 formula: a scale of 1 for an all-zero row.
 
 Everything here is written from the format definitions, not from a library
@@ -123,6 +128,20 @@ def fp8_quantize_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return fp8_code(y), scale
 
 
+def int8_quantize_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row int8 over the last axis: scale = f32(max|x| / 127) (IEEE f32 divide; 1
+    for an all-zero row), code = clamp(round_half_even(f32(x / scale)), -127, 127)."""
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("int8_quantize_rows: non-finite input")
+    a = np.max(np.abs(x), axis=-1)
+    scale = (a / np.float32(127.0)).astype(np.float32)
+    scale = np.where(a == 0, np.float32(1.0), scale).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
+    code = np.clip(np.rint(y), -127, 127).astype(np.int8)  # rint: round half to even
+    return code, scale
+
+
 def fp8_unscaled(x: np.ndarray) -> np.ndarray:
     """The pages' fp8 KV: code = RNE_e4m3fn(clamp(x, -448, 448)), no scale."""
     x = np.asarray(x, dtype=np.float32)
@@ -143,6 +162,8 @@ def encode_kv(x: np.ndarray, kv_dtype: str) -> tuple[np.ndarray, np.ndarray | No
         return fp8_quantize_rows(x)
     if kv_dtype == "fp8u":
         return fp8_unscaled(x), None
+    if kv_dtype == "int8":
+        return int8_quantize_rows(x)
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
@@ -156,7 +177,10 @@ def kv_values(raw: np.ndarray, scale: np.ndarray | None, kv_dtype: str) -> np.nd
         return fp8_value(raw) * np.asarray(scale, dtype=np.float64)[..., None]
     if kv_dtype == "fp8u":
         return fp8_value(raw)
+    if kv_dtype == "int8":
+        return np.asarray(raw, dtype=np.int8).astype(np.float64) * np.asarray(scale, dtype=np.float64)[..., None]
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
-RAW_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8u": np.uint8}
+RAW_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8u": np.uint8, "int8": np.int8}
+SCALED = ("fp8", "int8")  # dtypes stored with one f32 scale per (token, kv head)

@@ -58,7 +58,7 @@ class KVPool:
         nbytes = int(np.prod(shp)) * np.dtype(raw).itemsize
         self.k = np.frombuffer(bytearray([sentinel]) * nbytes, dtype=raw).reshape(shp).copy()
         self.v = self.k.copy()
-        if kv_dtype == "fp8":
+        if kv_dtype in enc.SCALED:
             sshp = (num_pages, num_kv_heads, page_size)
             sb = bytearray([sentinel]) * (int(np.prod(sshp)) * 4)
             self.k_scale = np.frombuffer(sb, dtype=np.float32).reshape(sshp).copy()
@@ -113,7 +113,7 @@ class KVPool:
         off = j % S
         k = self.k[pages, :, off, :]
         v = self.v[pages, :, off, :]
-        if self.kv_dtype == "fp8":
+        if self.kv_dtype in enc.SCALED:
             return k, v, self.k_scale[pages, :, off], self.v_scale[pages, :, off]
         return k, v, None, None
 
@@ -375,7 +375,7 @@ def ring_values(pool: KVPool, ring_row: np.ndarray, slots_idx: list[int]):
     off = idx % S
     k, v = pool.k[pages, :, off, :], pool.v[pages, :, off, :]
     ks = vs = None
-    if pool.kv_dtype == "fp8":
+    if pool.kv_dtype in enc.SCALED:
         ks, vs = pool.k_scale[pages, :, off], pool.v_scale[pages, :, off]
     return enc.kv_values(k, ks, pool.kv_dtype), enc.kv_values(v, vs, pool.kv_dtype)
 

@@ -66,7 +66,7 @@ def brute_attention(q, K, V, p, window, scale):
 
 
 # ------------------------------------------------- brute force, dense copy
-@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u", "int8"])
 def test_decode_matches_brute_force_over_contiguous_copy(kv_dtype):
     wl = W.custom_decode(101, [1, 5, 17, 33], 4, 2, 8, 4, kv_dtype, spare_pages=3)
     pool = build_decode_pool(wl)
@@ -156,7 +156,7 @@ def test_visible_range_definition():
 
 
 # ------------------------------------------------------------------ writes
-@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u", "int8"])
 def test_slot_minus_one_never_writes_and_others_land(kv_dtype):
     pool = KVPool(6, 4, 2, 8, kv_dtype, sentinel=0xA5)
     before = pool.pool_bytes()

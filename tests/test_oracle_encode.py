@@ -210,3 +210,32 @@ def test_fp8_unscaled_is_the_nearest_code_of_the_clamped_value():
     assert codes[-6] == 0x7E and codes[-5] == 0xFE  # 1e6 and -1e6 saturate to +-448
     raw, sc = E.encode_kv(x.reshape(-1, 1), "fp8u")
     assert sc is None and np.array_equal(E.kv_values(raw, None, "fp8u").reshape(-1), E.fp8_value(codes))
+
+
+def test_int8_rows_follow_the_formula_by_plain_python():
+    """int8 KV rows (the pages' int8 formula per (token, kv head) row): recomputed with
+    Python floats and round() (ties to even), independent of numpy's rint; the absmax
+    element maps to +-127 exactly; an all-zero row has scale 1 and codes 0."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((300, 64)) * rng.choice([1e-3, 1.0, 50.0], (300, 1))).astype(np.float32)
+    x[5] = 0.0
+    x[7, :4] = [2.5, -2.5, 1.0, 0.5]  # exact ties after the divide when absmax = 127 * 2^k
+    x[7, 4:] = 0.0
+    x[7, 10] = 127.0 / 64
+    codes, scale = E.int8_quantize_rows(x)
+    for r in range(x.shape[0]):
+        a = max(abs(float(v)) for v in x[r])
+        s = np.float32(1.0) if a == 0 else np.float32(np.float32(a) / np.float32(127.0))
+        assert scale[r] == s
+        for d in range(x.shape[1]):
+            y = float(np.float32(x[r, d] / s))
+            want = max(-127, min(127, round(y)))  # Python's round: half to even
+            assert codes[r, d] == want, (r, d, x[r, d], y, codes[r, d], want)
+        if a > 0:
+            i = int(np.argmax(np.abs(x[r])))
+            assert abs(int(codes[r, i])) == 127
+    assert scale[5] == 1.0 and np.all(codes[5] == 0)
+    raw, sc = E.encode_kv(x, "int8")
+    assert raw.dtype == np.int8 and np.array_equal(raw, codes) and np.array_equal(sc, scale)
+    v = E.kv_values(raw, sc, "int8")
+    assert np.all(np.abs(v - x) <= scale[:, None].astype(np.float64) * 0.5 + 1e-12)
