@@ -314,7 +314,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="c2,c3,c4,c4w,c5,c2r,c5u",
+    ap.add_argument("--configs", default="c2,c3,c4,c4w,c5,c2r,c5u,c2i",
                     help="comma list; the first is the headline (default c2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -39,11 +39,11 @@
  *
  * Pool layout (one layer; K and V are separate arrays, "numBlocks pages of
  * blockSize tokens, for K and for V", section 3 manifest bullets):
- *   x        = 16 / bytes(dtype)  elements per 16-byte chunk (f32 4, bf16 8, both fp8 16)
+ *   x        = 16 / bytes(dtype)  elements per 16-byte chunk (f32 4, bf16 8, fp8 and int8 16)
  *   k        [num_pages][num_kv_heads][head_dim / x][page_size][x]   of dtype
  *   v        [num_pages][num_kv_heads][page_size][head_dim]          of dtype
- *   k_scale  [num_pages][num_kv_heads][page_size]  f32  (TL_KV_FP8_E4M3 only, else NULL)
- *   v_scale  [num_pages][num_kv_heads][page_size]  f32  (TL_KV_FP8_E4M3 only, else NULL)
+ *   k_scale  [num_pages][num_kv_heads][page_size]  f32  (TL_KV_FP8_E4M3, TL_KV_INT8; else NULL)
+ *   v_scale  [num_pages][num_kv_heads][page_size]  f32  (TL_KV_FP8_E4M3, TL_KV_INT8; else NULL)
  * Slot s names page s / page_size, offset s % page_size.  Position j of sequence
  * b lives on page block_tables[b][j / page_size] at offset j % page_size.
  *
@@ -59,6 +59,12 @@
  *                   paragraph): code_d = RNE_e4m3fn(clamp(x_d, -448, 448)), no
  *                   scale (k_scale and v_scale are not used and may be NULL); a value
  *                   beyond +-448 saturates.  Value = code.
+ *   TL_KV_INT8      int8 codes with one f32 scale per (token, kv head), the pages'
+ *                   int8 formula applied per row (section 6, "Int8 weights"; the
+ *                   pages list int8 KV pools as not built): scale = f32(max_d |x_d|
+ *                   / 127) (1 for an all-zero row), code_d = clamp(round_half_even(
+ *                   f32(x_d / scale)), -127, 127), IEEE f32 divisions.  Value =
+ *                   code * scale.
  */
 #ifndef TL_H
 #define TL_H
@@ -78,14 +84,20 @@ typedef enum {
   TL_ERR_HIP = -4           /* a HIP runtime call failed (message in tl_last_error) */
 } tl_status;
 
-typedef enum { TL_KV_F32 = 0, TL_KV_BF16 = 1, TL_KV_FP8_E4M3 = 2, TL_KV_FP8_E4M3_UNSCALED = 3 } tl_kv_dtype;
+typedef enum {
+  TL_KV_F32 = 0,
+  TL_KV_BF16 = 1,
+  TL_KV_FP8_E4M3 = 2,
+  TL_KV_FP8_E4M3_UNSCALED = 3,
+  TL_KV_INT8 = 4
+} tl_kv_dtype;
 
 /* One layer's page pool.  The struct itself is a host object read during the call. */
 typedef struct {
   void* k;         /* device, layout above */
   void* v;         /* device, layout above */
-  float* k_scale;  /* device, TL_KV_FP8_E4M3 only */
-  float* v_scale;  /* device, TL_KV_FP8_E4M3 only */
+  float* k_scale;  /* device, TL_KV_FP8_E4M3 and TL_KV_INT8 only */
+  float* v_scale;  /* device, TL_KV_FP8_E4M3 and TL_KV_INT8 only */
   int32_t dtype;   /* tl_kv_dtype */
   int32_t num_pages;
   int32_t page_size;
@@ -201,7 +213,7 @@ int tl_paged_attn_prefill_ring(const tl_kv_pool* pool, const float* q, int32_t n
  * ("How serving works in Tlaloc", section 2: the pages a block table names).
  *   block_table_row  [>= ceil(length / page_size)] int32 (device)
  *   k_out, v_out     [length][num_kv_heads][head_dim] of the pool dtype (device)
- *   k_scale_out, v_scale_out  [length][num_kv_heads] f32 (TL_KV_FP8_E4M3 only, else NULL)
+ *   k_scale_out, v_scale_out  [length][num_kv_heads] f32 (scaled pools only, else NULL)
  */
 int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t length,
                  void* k_out, void* v_out, float* k_scale_out, float* v_scale_out,

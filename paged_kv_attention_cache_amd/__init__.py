@@ -20,8 +20,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # TL_LIBRARY may point at another build of the same ABI (e.g. a tuning variant)
 LIB_PATH = os.environ.get("TL_LIBRARY") or os.path.join(HERE, "libtl.so")
 
-KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8u": 3}  # fp8: per-(token, head) scales; fp8u: none
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1}
+# fp8 and int8: one f32 scale per (token, kv head); fp8u: the unscaled fp8 pool
+KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8u": 3, "int8": 4}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1, "int8": 1}
+SCALED = ("fp8", "int8")
 
 TL_OK, TL_ERR_INVALID, TL_ERR_UNSUPPORTED, TL_ERR_WORKSPACE, TL_ERR_HIP = 0, -1, -2, -3, -4
 
@@ -113,13 +115,14 @@ class KVPool:
                  device="cuda", fill_byte: int | None = None) -> "KVPool":
         import torch
         x = 16 // ELEM_BYTES[kv_dtype]
-        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "fp8u": torch.uint8}[kv_dtype]
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "fp8u": torch.uint8,
+               "int8": torch.int8}[kv_dtype]
         kshape = (num_pages, num_kv_heads, head_dim // x, page_size, x)
         vshape = (num_pages, num_kv_heads, page_size, head_dim)
         mk = (lambda s, dt: torch.empty(s, dtype=dt, device=device))
         k, v = mk(kshape, tdt), mk(vshape, tdt)
         ks = vs = None
-        if kv_dtype == "fp8":
+        if kv_dtype in SCALED:
             ks = mk((num_pages, num_kv_heads, page_size), torch.float32)
             vs = mk((num_pages, num_kv_heads, page_size), torch.float32)
         pool = KVPool(k, v, ks, vs, kv_dtype, num_pages, page_size, num_kv_heads, head_dim)
@@ -264,7 +267,7 @@ def tl_kv_gather(pool: KVPool, block_table_row, length: int, stream=None):
     k = torch.empty(shp, dtype=pool.k.dtype, device=dev)
     v = torch.empty(shp, dtype=pool.v.dtype, device=dev)
     ks = vs = None
-    if pool.kv_dtype == "fp8":
+    if pool.kv_dtype in SCALED:
         ks = torch.empty((length, pool.num_kv_heads), dtype=torch.float32, device=dev)
         vs = torch.empty((length, pool.num_kv_heads), dtype=torch.float32, device=dev)
     ps = pool.c_struct()

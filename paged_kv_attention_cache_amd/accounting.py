@@ -19,7 +19,8 @@ import math
 
 import numpy as np
 
-BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1}  # fp8u: the unscaled fp8 pool
+BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1, "int8": 1}  # fp8u: the unscaled fp8 pool
+SCALED = ("fp8", "int8")  # one f32 scale per (token, kv head) for K and for V
 
 
 # ----------------------------------------------------- page-level formulas
@@ -90,7 +91,7 @@ def decode_bytes(seq_lens, num_q_heads: int, kv_heads: int, head_dim: int, page_
     L = np.asarray(seq_lens, dtype=np.int64)
     vis = visible_counts(L - 1, window)
     kv = int(vis.sum()) * kv_heads * head_dim * 2 * BYTES[kv_dtype]
-    if kv_dtype == "fp8":
+    if kv_dtype in SCALED:
         kv += int(vis.sum()) * kv_heads * 2 * 4
     B = len(L)
     qo = 2 * B * num_q_heads * head_dim * 4
@@ -103,7 +104,7 @@ def write_bytes(slots, kv_heads: int, head_dim: int, kv_dtype: str) -> int:
     s = np.asarray(slots)
     live = int(np.count_nonzero(s != -1))
     b = live * kv_heads * head_dim * 2 * (4 + BYTES[kv_dtype])
-    if kv_dtype == "fp8":
+    if kv_dtype in SCALED:
         b += live * kv_heads * 2 * 4
     return b + 4 * s.size
 

@@ -45,13 +45,13 @@ bool validate_mode() {
 
 int check_pool(const char* fn, const tl_kv_pool* pool) {
   if (!pool) return fail(TL_ERR_INVALID, "%s: pool is NULL", fn);
-  if (pool->dtype < TL_KV_F32 || pool->dtype > TL_KV_FP8_E4M3_UNSCALED)
+  if (pool->dtype < TL_KV_F32 || pool->dtype > TL_KV_INT8)
     return fail(TL_ERR_UNSUPPORTED, "%s: pool->dtype (%d) is not a tl_kv_dtype", fn, pool->dtype);
   if (!pool->k) return fail(TL_ERR_INVALID, "%s: pool->k is NULL", fn);
   if (!pool->v) return fail(TL_ERR_INVALID, "%s: pool->v is NULL", fn);
   if (!aligned(pool->k, 16)) return fail(TL_ERR_INVALID, "%s: pool->k is not 16-byte aligned", fn);
   if (!aligned(pool->v, 16)) return fail(TL_ERR_INVALID, "%s: pool->v is not 16-byte aligned", fn);
-  if (pool->dtype == TL_KV_FP8_E4M3) {
+  if (pool->dtype == TL_KV_FP8_E4M3 || pool->dtype == TL_KV_INT8) {
     if (!pool->k_scale) return fail(TL_ERR_INVALID, "%s: pool->k_scale is NULL for a scaled fp8 pool", fn);
     if (!pool->v_scale) return fail(TL_ERR_INVALID, "%s: pool->v_scale is NULL for a scaled fp8 pool", fn);
     if (!aligned(pool->k_scale, 16)) return fail(TL_ERR_INVALID, "%s: pool->k_scale is not 16-byte aligned", fn);
@@ -390,7 +390,7 @@ int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t
   if (!k_out) return fail(TL_ERR_INVALID, "%s: k_out is NULL", fn);
   if (!v_out) return fail(TL_ERR_INVALID, "%s: v_out is NULL", fn);
   if (!aligned(k_out, 16) || !aligned(v_out, 16)) return fail(TL_ERR_INVALID, "%s: k_out/v_out not 16-byte aligned", fn);
-  if (pool->dtype == TL_KV_FP8_E4M3 && (!k_scale_out || !v_scale_out))
+  if ((pool->dtype == TL_KV_FP8_E4M3 || pool->dtype == TL_KV_INT8) && (!k_scale_out || !v_scale_out))
     return fail(TL_ERR_INVALID, "%s: k_scale_out/v_scale_out are NULL for a scaled fp8 pool", fn);
   hipStream_t s = (hipStream_t)stream;
   tl::GatherArgs a;

@@ -13,15 +13,16 @@ namespace tl {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP8U = 3 };
-constexpr bool kv_fp8(int k) { return k == KV_FP8 || k == KV_FP8U; }  // e4m3fn codes
-constexpr bool kv_scaled(int k) { return k == KV_FP8; }               // with (token, head) scales
+enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP8U = 3, KV_INT8 = 4 };
+constexpr bool kv_fp8(int k) { return k == KV_FP8 || k == KV_FP8U; }      // e4m3fn codes
+constexpr bool kv_scaled(int k) { return k == KV_FP8 || k == KV_INT8; }   // with (token, head) scales
 
 template <int KVT> struct KvTraits;
 template <> struct KvTraits<KV_F32> { typedef float T; static constexpr int BYTES = 4; static constexpr int X = 4; };
 template <> struct KvTraits<KV_BF16> { typedef uint16_t T; static constexpr int BYTES = 2; static constexpr int X = 8; };
 template <> struct KvTraits<KV_FP8> { typedef uint8_t T; static constexpr int BYTES = 1; static constexpr int X = 16; };
 template <> struct KvTraits<KV_FP8U> : KvTraits<KV_FP8> {};
+template <> struct KvTraits<KV_INT8> : KvTraits<KV_FP8> {};
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int KEY_BLOCK = 2048;  // the pages' key-block width; loop bounds are taken per block
@@ -46,6 +47,12 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
 }
 
+// four int8 codes packed in a dword -> four f32 (exact)
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (float)(int8_t)(w >> (8 * i));  // sign-extended byte i
+}
+
 // widen one 16-byte chunk of stored elements to f32 (X values)
 template <int KVT>
 __device__ __forceinline__ void widen_chunk(const uint4& c, float* o) {
@@ -55,6 +62,8 @@ __device__ __forceinline__ void widen_chunk(const uint4& c, float* o) {
   } else if constexpr (KVT == KV_BF16) {
     o[0] = bf16_lo(c.x); o[1] = bf16_hi(c.x); o[2] = bf16_lo(c.y); o[3] = bf16_hi(c.y);
     o[4] = bf16_lo(c.z); o[5] = bf16_hi(c.z); o[6] = bf16_lo(c.w); o[7] = bf16_hi(c.w);
+  } else if constexpr (KVT == KV_INT8) {
+    i8x4_to_f32(c.x, o); i8x4_to_f32(c.y, o + 4); i8x4_to_f32(c.z, o + 8); i8x4_to_f32(c.w, o + 12);
   } else {
     fp8x4_to_f32(c.x, o); fp8x4_to_f32(c.y, o + 4); fp8x4_to_f32(c.z, o + 8); fp8x4_to_f32(c.w, o + 12);
   }

@@ -297,7 +297,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t s) {
     case KV_F32: return prefill_dispatch<KV_F32>(a, s);
     case KV_BF16: return prefill_dispatch<KV_BF16>(a, s);
     case KV_FP8: return prefill_dispatch<KV_FP8>(a, s);
-    default: return prefill_dispatch<KV_FP8U>(a, s);
+    case KV_FP8U: return prefill_dispatch<KV_FP8U>(a, s);
+    default: return prefill_dispatch<KV_INT8>(a, s);
   }
 }
 

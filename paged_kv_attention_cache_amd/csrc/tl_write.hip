@@ -44,6 +44,21 @@ __device__ __forceinline__ void encode_row(const float (&x)[D / ROW_LANES], type
   } else if constexpr (KVT == KV_BF16) {
 #pragma unroll
     for (int i = 0; i < E; ++i) enc[i] = (uint16_t)f32_to_bf16(x[i]);
+  } else if constexpr (KVT == KV_INT8) {
+    // the int8 formula per row: scale = absmax / 127 (1 for a zero row), codes rounded
+    // half to even and clamped to +-127, both divisions IEEE f32
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(x[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    scale = (m == 0.0f) ? 1.0f : m / 127.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float y = fminf(fmaxf(__builtin_rintf(x[i] / scale), -127.0f), 127.0f);
+      enc[i] = (uint8_t)(int8_t)(int)y;
+    }
   } else if constexpr (KVT == KV_FP8U) {
     // no scale: the value itself, saturated at +-448, to the nearest code
 #pragma unroll
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(WG) void write_kernel(WriteArgs a) {
   // instruction of the 8 lanes covers one contiguous span of the destination.
   constexpr int UE = (X * ROW_LANES <= D) ? X : D / ROW_LANES;
   constexpr int NU = E / UE;  // units per lane
-  constexpr bool NTL = !kv_fp8(KVT), NTS = kv_fp8(KVT);
+  constexpr bool NTL = Tr::BYTES != 1, NTS = Tr::BYTES == 1;
   float xk[E], xv[E];
   {
     const u4* sk = reinterpret_cast<const u4*>(a.k_new + row * D);
@@ -224,7 +239,8 @@ hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s) {
     case KV_F32: return write_dispatch<KV_F32>(a, s);
     case KV_BF16: return write_dispatch<KV_BF16>(a, s);
     case KV_FP8: return write_dispatch<KV_FP8>(a, s);
-    default: return write_dispatch<KV_FP8U>(a, s);
+    case KV_FP8U: return write_dispatch<KV_FP8U>(a, s);
+    default: return write_dispatch<KV_INT8>(a, s);
   }
 }
 
@@ -234,7 +250,8 @@ hipError_t launch_gather(const GatherArgs& a, int kv_dtype, hipStream_t s) {
     case KV_F32: return gather_dispatch<KV_F32>(a, s);
     case KV_BF16: return gather_dispatch<KV_BF16>(a, s);
     case KV_FP8: return gather_dispatch<KV_FP8>(a, s);
-    default: return gather_dispatch<KV_FP8U>(a, s);
+    case KV_FP8U: return gather_dispatch<KV_FP8U>(a, s);
+    default: return gather_dispatch<KV_INT8>(a, s);
   }
 }
 

@@ -104,8 +104,9 @@ def pool_logical(pool: KVPool):
     """Pool contents as numpy raw arrays in logical [P, H, S, D] order (+ scales)."""
     import torch
     k = pool.k.permute(0, 1, 3, 2, 4).reshape(pool.num_pages, pool.num_kv_heads, pool.page_size, pool.head_dim)
-    raw = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8, "fp8u": torch.uint8}[pool.kv_dtype]
-    npdt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8u": np.uint8}[pool.kv_dtype]
+    raw = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8, "fp8u": torch.uint8,
+           "int8": torch.int8}[pool.kv_dtype]
+    npdt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8u": np.uint8, "int8": np.int8}[pool.kv_dtype]
     kk = k.contiguous().view(raw).cpu().numpy().view(npdt)
     vv = pool.v.contiguous().view(raw).cpu().numpy().view(npdt)
     ks = vs = None

@@ -53,7 +53,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    kv_dtype: str  # "f32" | "bf16" | "fp8" (scaled) | "fp8u" (unscaled)
+    kv_dtype: str  # "f32" | "bf16" | "fp8" (scaled) | "fp8u" (unscaled) | "int8" (scaled)
     window: int = 0  # <= 0: full attention
     seq_lens: np.ndarray | None = None  # decode: [B] int32, incl. the new token
     tokens_per_row: int = 0  # prefill: T
@@ -255,6 +255,15 @@ def llama3_decode(batch: int = 64, lo: int = 512, hi: int = 8192) -> Workload:
     return wl
 
 
+def llama3_decode_int8(batch: int = 64, lo: int = 512, hi: int = 8192) -> Workload:
+    """The c2 decode layer (same lengths) on an int8 KV pool with per-(token, head) scales."""
+    rng = np.random.default_rng([SEED, 2, T_LENGTHS, 0])  # the same lengths as c2
+    lens = rng.integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+    wl = Workload("c2i_llama3_decode_int8", 8, "decode", batch, 32, 8, 128, 16, "int8", seq_lens=lens)
+    _assign_pages(wl, lens.tolist())
+    return wl
+
+
 def llama3_decode_ring(batch: int = 64, lo: int = 512, hi: int = 8192, window: int = 2048) -> Workload:
     """The c2 decode layer as a sliding-window layer on a windowed pool: window 2,048,
     rings of ceil(2048/16) + 1 = 129 pages (section 3's default of one spare page)."""
@@ -315,6 +324,7 @@ CONFIGS = {
     "c5": fp8_decode,
     "c2r": llama3_decode_ring,
     "c5u": fp8_unscaled_decode,
+    "c2i": llama3_decode_int8,
 }
 
 

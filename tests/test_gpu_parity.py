@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 # fp8u (the unscaled fp8 pool) stores values that widen exactly, so its outputs are
 # held to the f32 bound; scaled fp8 is compared with the dequantised oracle at 1e-2.
-TOL = {"f32": 2e-5, "bf16": 2e-5, "fp8": 1e-2, "fp8u": 2e-5}
+TOL = {"f32": 2e-5, "bf16": 2e-5, "fp8": 1e-2, "fp8u": 2e-5, "int8": 2e-5}
 
 
 @pytest.fixture(scope="module")
@@ -53,7 +53,7 @@ def assert_pool_equal(gpu_pool, opool):
 
 
 # ====================================================================== writes
-@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u"])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u", "int8"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_write_bit_exact_with_sentinels(torch_cuda, kv_dtype, D):
     torch = torch_cuda
@@ -129,7 +129,7 @@ def test_bf16_write_matches_oracle_on_tie_strata(torch_cuda):
     assert np.array_equal(vv.reshape(P * S, D)[:n], want)
 
 
-@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u"])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8", "fp8u", "int8"])
 def test_gather_bit_exact(torch_cuda, kv_dtype):
     torch = torch_cuda
     import paged_kv_attention_cache_amd as tl
@@ -146,7 +146,7 @@ def test_gather_bit_exact(torch_cuda, kv_dtype):
         ok, ov, oks, ovs = op.gather_raw(wl.block_tables[b], L)
         assert np.array_equal(k.cpu().view(torch.uint8).numpy().reshape(-1), ok.view(np.uint8).reshape(-1))
         assert np.array_equal(v.cpu().view(torch.uint8).numpy().reshape(-1), ov.view(np.uint8).reshape(-1))
-        if kv_dtype == "fp8":
+        if kv_dtype in ("fp8", "int8"):
             assert np.array_equal(ks.cpu().numpy(), oks) and np.array_equal(vs.cpu().numpy(), ovs)
 
 
@@ -169,6 +169,9 @@ DECODE_CASES = [
     ("g8_fp8u_exact_split", [1, 300, 4095, 4097, 9000], 16, 2, 128, 64, "fp8u", 0),
     ("g4_fp8u_window", [3000, 700, 5], 8, 2, 128, 16, "fp8u", 900),
     ("g2_fp8u_d64_page8", [9, 700], 4, 2, 64, 8, "fp8u", 0),
+    ("g4_int8", [1, 513, 3000], 8, 2, 128, 16, "int8", 0),
+    ("g8_int8_window", [4097, 900], 16, 2, 128, 64, "int8", 1000),
+    ("g1_int8_d64", [70, 5], 4, 4, 64, 16, "int8", 0),
 ]
 
 
@@ -266,6 +269,7 @@ PREFILL_CASES = [
     ("window_longer_than_context", [30], [5], 32, 8, 2, 128, 16, "bf16", 5000),
     ("g4_d64_window1", [20], [3], 20, 8, 2, 64, 8, "bf16", 1),
     ("g8_fp8u_history", [45, 3], [70, 0], 48, 16, 2, 128, 16, "fp8u", 0),
+    ("g4_int8_history", [40, 7], [33, 100], 48, 8, 2, 128, 16, "int8", 0),
 ]
 
 
@@ -405,3 +409,33 @@ def test_fp8u_write_saturates_and_rounds_like_the_oracle(torch_cuda):
     want = E.fp8_unscaled(k.reshape(n, D))
     assert np.array_equal(kk.reshape(P * S, D)[:n], want)
     assert np.array_equal(vv.reshape(P * S, D)[:n], want)
+
+
+def test_int8_write_rounds_half_to_even_like_the_oracle(torch_cuda):
+    """int8 rows whose quotients land exactly on halves (absmax 127 * 2^k makes the
+    scale 2^k, so x / scale is exact), plus random rows: codes, scales bit for bit."""
+    torch = torch_cuda
+    import paged_kv_attention_cache_amd as tl
+    D, H, S = 64, 1, 16
+    rng = np.random.default_rng(44)
+    rows = []
+    for k in (-3, 0, 2):
+        halves = (np.arange(-126, 127) + 0.5) * 2.0 ** k
+        for a in range(0, len(halves), D - 1):
+            r = np.zeros(D, np.float32)
+            part = halves[a:a + D - 1]
+            r[:len(part)] = part
+            r[-1] = 127 * 2.0 ** k  # absmax -> scale 2^k
+            rows.append(r)
+    rows += list((rng.standard_normal((40, D)) * 3).astype(np.float32))
+    x = np.stack(rows).astype(np.float32).reshape(-1, H, D)
+    n = x.shape[0]
+    P = (n + S - 1) // S
+    gp = tl.KVPool.allocate(P, S, H, D, "int8", fill_byte=0)
+    t = torch.from_numpy(x).cuda()
+    tl.tl_kv_cache_write(gp, t, t, torch.arange(n, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    kk, _, ks, _ = R.pool_logical(gp)
+    codes, scale = E.int8_quantize_rows(x.reshape(n, D))
+    assert np.array_equal(kk.reshape(P * S, D)[:n], codes)
+    assert np.array_equal(ks.reshape(-1)[:n], scale)

@@ -74,6 +74,7 @@ RING_DECODE_CASES = [
     ("bf16_g8_window_one", [1, 77], 16, 2, 128, 16, "bf16", 1, 1),
     ("bf16_wide_ring_many_splits", [2500, 7000], 8, 2, 128, 16, "bf16", 120, 1800),
     ("fp8u_g8_exact_split", [10, 700, 5000], 16, 2, 128, 16, "fp8u", 40, 600),
+    ("int8_g4", [30, 2000], 8, 2, 128, 16, "int8", 10, 150),
 ]
 
 
