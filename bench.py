@@ -120,6 +120,41 @@ def run_config(name: str, steps: int, warmup: int):
     return wl, res
 
 
+def run_gdn(name: str, steps: int, warmup: int):
+    """GATED_DELTA_RULE decode steps over the workload's state pool (each step reads and
+    writes every live row's [H, 128, 128] f32 state): KV-style GB/s of the call."""
+    import torch
+    from paged_kv_attention_cache_amd import tl_gated_delta_rule_decode
+    from paged_kv_attention_cache_amd import workloads as W
+    wl = W.make(name)
+    pool = torch.from_numpy(wl.initial_pool()).cuda()
+    slots, pos = wl.slots_positions()
+    ins = [torch.from_numpy(x).cuda() for x in wl.step_inputs(0)]
+    st, pt = torch.from_numpy(slots).cuda(), torch.from_numpy(pos).cuda()
+    out = torch.empty_like(ins[2])
+    for _ in range(warmup):
+        tl_gated_delta_rule_decode(pool, *ins, st, pt, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        tl_gated_delta_rule_decode(pool, *ins, st, pt, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    live = int(np.count_nonzero(slots >= 0))
+    fresh = int(np.count_nonzero((slots >= 0) & (pos == 0)))
+    D, H = wl.head_dim, wl.num_heads
+    # state read (not for fresh rows) and written, q k v read and o written, g and beta, slots, positions
+    nbytes = (live * 2 - fresh) * H * D * D * 4 + wl.batch * H * (4 * D * 4 + 8) + wl.batch * 8
+    return wl, {"kind": "gdn", "workload": wl.name, "attn_ms": ms, "attn_bytes": nbytes,
+                "attn_GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "ms_per_step": wall * 1e3 / steps}
+
+
 def history_write_rate(wl, pool, reps: int = 10):
     """KV_CACHE_WRITE throughput on the workload's first history chunk (up to 64K tokens):
     the same rows rewritten to the same slots, timed with HIP events."""
@@ -314,7 +349,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="c2,c3,c4,c4w,c5,c2r,c5u,c2i",
+    ap.add_argument("--configs", default="c2,c3,c4,c4w,c5,c2r,c5u,c2i,c6",
                     help="comma list; the first is the headline (default c2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -333,7 +368,7 @@ def main():
     names = [c.strip() for c in args.configs.split(",") if c.strip()]
     results = {}
     for n in names:
-        wl, r = run_config(n, args.steps, args.warmup)
+        wl, r = run_gdn(n, args.steps, args.warmup) if n == "c6" else run_config(n, args.steps, args.warmup)
         results[n] = (wl, r)
         log(f"[bench] {n}: " + json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}))
 

@@ -208,6 +208,28 @@ int tl_paged_attn_prefill_ring(const tl_kv_pool* pool, const float* q, int32_t n
                                size_t workspace_bytes, void* stream);
 
 /*
+ * GATED_DELTA_RULE, decode step ("How serving works in Tlaloc", "Linear-attention
+ * layers: the state pools"): a Gated DeltaNet layer keeps per sequence an f32
+ * recurrent state [num_heads][128][128] in a pool indexed by the sequence's state
+ * slot.  For each row b with slot s = state_slots[b] and each head h, with S the
+ * state (S[i][j]: i over the key dimension, j over the value dimension):
+ *     S = S * exp(g);  S += k (outer) beta (v - k^T S);  o = q^T S  (the updated S)
+ * and S is written back to the pool in place.  A row at position 0 starts from zero
+ * state (the slot's old contents are not read); slot -1 is a pad: nothing is read or
+ * written and its output row is 0.  Rows of one call must hold distinct slots.
+ *   state_pool   [num_slots][num_heads][128][128] f32 (device, updated in place)
+ *   q, k, v      [batch][num_heads][128] f32;  g, beta [batch][num_heads] f32
+ *                (g is the log decay; q, k, v are used as given)
+ *   state_slots  [batch] int32;  positions [batch] int32 (the row's position)
+ *   out          [batch][num_heads][128] f32
+ * head_dim must be 128.  f32 operands, products and sums.
+ */
+int tl_gated_delta_rule_decode(float* state_pool, int32_t num_slots, int32_t num_heads,
+                               int32_t head_dim, const float* q, const float* k, const float* v,
+                               const float* g, const float* beta, const int32_t* state_slots,
+                               const int32_t* positions, int32_t batch, float* out, void* stream);
+
+/*
  * Copy sequence positions 0..length-1 out of the pool in logical order, as stored
  * (no decoding), so that a test can compare written/gathered KV byte for byte
  * ("How serving works in Tlaloc", section 2: the pages a block table names).

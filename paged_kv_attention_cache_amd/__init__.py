@@ -65,10 +65,11 @@ def lib() -> ctypes.CDLL:
         L.tl_paged_attn_decode_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp, sz, vp]
         L.tl_paged_attn_prefill_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
         L.tl_kv_gather.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
+        L.tl_gated_delta_rule_decode.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         L.tl_last_error.restype = ctypes.c_char_p
         L.tl_abi_version.restype = ctypes.c_int
         for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather",
-                   "tl_paged_attn_decode_ring", "tl_paged_attn_prefill_ring"):
+                   "tl_paged_attn_decode_ring", "tl_paged_attn_prefill_ring", "tl_gated_delta_rule_decode"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -257,6 +258,20 @@ def ring_slot_mapping(ring_row, positions, page_size: int):
     pc = np.maximum(p, 0)
     slots = ring_row[(pc // page_size) % len(ring_row)] * page_size + pc % page_size
     return np.where(p < 0, -1, slots).astype(np.int32)
+
+
+def tl_gated_delta_rule_decode(state_pool, q, k, v, g, beta, state_slots, positions, out=None, stream=None):
+    """GATED_DELTA_RULE decode step: state_pool f32 [num_slots, H, 128, 128] (updated in
+    place); q, k, v f32 [B, H, 128]; g, beta f32 [B, H]; state_slots, positions int32 [B]."""
+    import torch
+    B, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib().tl_gated_delta_rule_decode(state_pool.data_ptr(), int(state_pool.shape[0]), H, D, q.data_ptr(),
+                                            k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                            state_slots.data_ptr(), positions.data_ptr(), B, out.data_ptr(),
+                                            _stream(stream)))
+    return out
 
 
 def tl_kv_gather(pool: KVPool, block_table_row, length: int, stream=None):

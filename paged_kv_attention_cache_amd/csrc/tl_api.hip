@@ -379,6 +379,52 @@ int tl_paged_attn_prefill_ring(const tl_kv_pool* pool, const float* q, int32_t n
                         tokens_per_row, window, scale, out, stream);
 }
 
+int tl_gated_delta_rule_decode(float* state_pool, int32_t num_slots, int32_t num_heads, int32_t head_dim,
+                               const float* q, const float* k, const float* v, const float* g, const float* beta,
+                               const int32_t* state_slots, const int32_t* positions, int32_t batch, float* out,
+                               void* stream) {
+  const char* fn = "tl_gated_delta_rule_decode";
+  if (head_dim != 128) return fail(TL_ERR_UNSUPPORTED, "%s: head_dim (%d) must be 128", fn, head_dim);
+  if (num_heads <= 0) return fail(TL_ERR_INVALID, "%s: num_heads (%d) must be > 0", fn, num_heads);
+  if (num_slots <= 0) return fail(TL_ERR_INVALID, "%s: num_slots (%d) must be > 0", fn, num_slots);
+  if ((int64_t)num_slots * num_heads >= ((int64_t)1 << 31) / (128 * 128))
+    return fail(TL_ERR_UNSUPPORTED, "%s: num_slots * num_heads is too large", fn);
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if ((int64_t)batch * num_heads >= ((int64_t)1 << 31) / 128)
+    return fail(TL_ERR_UNSUPPORTED, "%s: batch * num_heads is too large for one call", fn);
+  if (batch == 0) return ok();
+  const void* ptrs[] = {state_pool, q, k, v, g, beta, state_slots, positions, out};
+  const char* names[] = {"state_pool", "q", "k", "v", "g", "beta", "state_slots", "positions", "out"};
+  for (int i = 0; i < 9; ++i) {
+    if (!ptrs[i]) return fail(TL_ERR_INVALID, "%s: %s is NULL", fn, names[i]);
+    if (!aligned(ptrs[i], (i < 4 || i == 8) ? 16 : 4))
+      return fail(TL_ERR_INVALID, "%s: %s is not %d-byte aligned", fn, names[i], (i < 4 || i == 8) ? 16 : 4);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int rc;
+  if (validate_mode()) {
+    std::vector<int32_t> sl;
+    if ((rc = copy_to_host(fn, "state_slots", state_slots, (size_t)batch, sl, s))) return rc;
+    std::vector<int32_t> used;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (sl[b] == -1) continue;
+      if (sl[b] < 0 || sl[b] >= num_slots)
+        return fail(TL_ERR_INVALID, "%s: state_slots[%d] = %d is outside the pool (TL_VALIDATE)", fn, b, sl[b]);
+      used.push_back(sl[b]);
+    }
+    std::sort(used.begin(), used.end());
+    for (size_t i = 1; i < used.size(); ++i)
+      if (used[i] == used[i - 1]) return fail(TL_ERR_INVALID, "%s: state slot %d appears twice (TL_VALIDATE)", fn, used[i]);
+  }
+  tl::GdnArgs a;
+  a.pool = state_pool; a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.slots = state_slots; a.positions = positions; a.out = out;
+  a.batch = batch; a.num_heads = num_heads; a.num_slots = num_slots;
+  hipError_t e = tl::launch_gdn_decode(a, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
 int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t length, void* k_out, void* v_out,
                  float* k_scale_out, float* v_scale_out, void* stream) {
   const char* fn = "tl_kv_gather";

@@ -146,6 +146,16 @@ struct PrefillArgs {
   float qscale;
 };
 
+// Gated DeltaNet decode step over a slot-indexed state pool
+struct GdnArgs {
+  float* pool;          // [num_slots][num_heads][128][128] f32, updated in place
+  const float *q, *k, *v, *g, *beta;  // [B][H][128] x3, [B][H] x2
+  const int32_t* slots;      // [B], -1 = pad
+  const int32_t* positions;  // [B], 0 = start from zero state
+  float* out;                // [B][H][128]
+  int batch, num_heads, num_slots;
+};
+
 // ------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are already validated.
 hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s);
@@ -154,5 +164,6 @@ int decode_split_keys(int kv_dtype, int group, int page_size);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s);
 int prefill_tokens_per_wg(int group);
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t s);
+hipError_t launch_gdn_decode(const GdnArgs& a, hipStream_t s);
 
 }  // namespace tl

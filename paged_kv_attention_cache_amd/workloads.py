@@ -315,6 +315,57 @@ def fp8_unscaled_decode(batch: int = 128, lo: int = 1024, hi: int = 32768) -> Wo
     return wl
 
 
+@dataclass
+class GdnWorkload:
+    """Inputs of one GATED_DELTA_RULE decode step over a slot-indexed state pool
+    ("How serving works in Tlaloc", "Linear-attention layers: the state pools").
+    Row b holds slot ``slots[b]`` (-1 = pad) at position ``positions[b]`` (0 = fresh
+    row, starts from zero state).  q and k are N(0, 1/128) (norm about 1), v N(0, 1),
+    g (log decay) U(-1, -0.01), beta U(0.05, 0.95); the pool starts N(0, 0.1^2)."""
+
+    name: str
+    cfg_id: int
+    batch: int
+    num_heads: int
+    num_slots: int
+    head_dim: int = 128
+    seed: int = SEED
+
+    def _rng(self, tensor_id: int) -> np.random.Generator:
+        return np.random.default_rng([self.seed, self.cfg_id, tensor_id, 0])
+
+    def slots_positions(self) -> tuple[np.ndarray, np.ndarray]:
+        rng = self._rng(T_PERM)
+        slots = rng.permutation(self.num_slots)[:self.batch].astype(np.int32)
+        positions = rng.integers(1, 32768, size=self.batch).astype(np.int32)
+        positions[::9] = 0                     # fresh rows: zero state whatever the slot holds
+        if self.batch > 3:
+            slots[3] = -1                      # a pad row
+        return slots, positions
+
+    def step_inputs(self, step: int = 0):
+        """q, k, v [B, H, D], g, beta [B, H] (f32) of decode step `step`."""
+        rng = np.random.default_rng([self.seed, self.cfg_id, T_Q, step])
+        shp = (self.batch, self.num_heads, self.head_dim)
+        sd = np.float32(1.0 / math.sqrt(self.head_dim))
+        q = (rng.standard_normal(shp, dtype=np.float32) * sd).astype(np.float32)
+        k = (rng.standard_normal(shp, dtype=np.float32) * sd).astype(np.float32)
+        v = rng.standard_normal(shp, dtype=np.float32)
+        g = rng.uniform(-1.0, -0.01, (self.batch, self.num_heads)).astype(np.float32)
+        beta = rng.uniform(0.05, 0.95, (self.batch, self.num_heads)).astype(np.float32)
+        return q, k, v, g, beta
+
+    def initial_pool(self) -> np.ndarray:
+        shp = (self.num_slots, self.num_heads, self.head_dim, self.head_dim)
+        return (self._rng(T_K).standard_normal(shp, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+
+
+def gdn_decode_layer(batch: int = 128, heads: int = 16, slots: int = 160) -> GdnWorkload:
+    """A Gated DeltaNet decode layer: 128 sequences, 16 heads of 128 x 128 f32 state,
+    a pool of 160 slots (128 KiB read and written per sequence and head)."""
+    return GdnWorkload("c6_gated_delta_rule_decode", 9, batch, heads, slots)
+
+
 CONFIGS = {
     "c1": tiny_decode,
     "c2": llama3_decode,
@@ -325,10 +376,11 @@ CONFIGS = {
     "c2r": llama3_decode_ring,
     "c5u": fp8_unscaled_decode,
     "c2i": llama3_decode_int8,
+    "c6": gdn_decode_layer,
 }
 
 
-def make(name: str) -> Workload:
+def make(name: str):
     return CONFIGS[name]()
 
 
