@@ -12,6 +12,6 @@ Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` to
 something other than itself (format definitions, closed forms, brute force,
 invariants the pages state, and the pages' printed byte counts).
 """
-from . import encode, gdn, paged  # noqa: F401
+from . import alloc, encode, gdn, paged  # noqa: F401
 from .paged import (KVPool, KEY_BLOCK, attend_rows, attend_rows_blockwise, decode, decode_ring,  # noqa: F401
                     prefill, prefill_ring, ring_slots)
