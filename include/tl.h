@@ -81,7 +81,8 @@ typedef enum {
   TL_ERR_INVALID = -1,      /* an argument is null, negative, misaligned or inconsistent */
   TL_ERR_UNSUPPORTED = -2,  /* a shape or dtype outside the supported set above */
   TL_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace_size query */
-  TL_ERR_HIP = -4           /* a HIP runtime call failed (message in tl_last_error) */
+  TL_ERR_HIP = -4,          /* a HIP runtime call failed (message in tl_last_error) */
+  TL_ERR_NO_PAGES = -5      /* the page allocator refused a request (message names the holders) */
 } tl_status;
 
 typedef enum {
@@ -228,6 +229,45 @@ int tl_gated_delta_rule_decode(float* state_pool, int32_t num_slots, int32_t num
                                int32_t head_dim, const float* q, const float* k, const float* v,
                                const float* g, const float* beta, const int32_t* state_slots,
                                const int32_t* positions, int32_t batch, float* out, void* stream);
+
+/*
+ * Host page allocator ("How serving works in Tlaloc": the runtime comparison table and
+ * the backend bullets of section 3; prefix sharing: the KV-cache management page,
+ * "Reuse identical causal prefixes" and the paragraph before it).  An opaque HOST
+ * object, not thread-safe.  Sequences are named by int64 ids; `now` is the caller's
+ * clock (any unit; idle_timeout in the same unit).
+ * - tl_alloc_start: a new sequence, holding no pages (an id already started is refused).
+ * - tl_alloc_append: room for n_tokens more positions.  Writes their slots (host
+ *   int32 [n_tokens], for tl_kv_cache_write) and at most one page copy (host int32
+ *   [1] each) that the caller must run with tl_kv_copy_pages BEFORE writing: a page
+ *   shared with a forked sequence and only partly filled is copied before this
+ *   sequence writes into it.  When pages run short, sequences idle past the timeout
+ *   (last activity < now - idle_timeout) are reclaimed, least recently active first
+ *   and only as many as needed, if they cover the shortage; otherwise the call returns
+ *   TL_ERR_NO_PAGES, tl_last_error() names the sequences holding pages, the request
+ *   changes nothing (its sequence keeps its pages) and counts as activity.  The lowest
+ *   free page is always taken first.
+ * - tl_alloc_fork: child shares parent's pages covering its first n_tokens positions
+ *   (reference counted); tl_alloc_end: releases a sequence's pages (a page returns to
+ *   the free list when no sequence holds it).
+ * - tl_alloc_tables: block tables [n][max_blocks] (-1 past a sequence's pages) and
+ *   lengths [n] of the given sequences, host arrays, for the attention entries.
+ * - tl_kv_copy_pages: device copy of whole pages src_pages[i] -> dst_pages[i] (K, V
+ *   and, for scaled pools, scales), n <= 65535; device int32 arrays.
+ */
+typedef struct tl_page_allocator tl_page_allocator;
+tl_page_allocator* tl_alloc_create(int32_t num_pages, int32_t page_size, double idle_timeout);
+void tl_alloc_destroy(tl_page_allocator* a);
+int32_t tl_alloc_free_pages(const tl_page_allocator* a);
+int tl_alloc_start(tl_page_allocator* a, int64_t seq, double now);
+int tl_alloc_end(tl_page_allocator* a, int64_t seq);
+int tl_alloc_fork(tl_page_allocator* a, int64_t parent, int64_t child, int64_t n_tokens, double now);
+int tl_alloc_append(tl_page_allocator* a, int64_t seq, int32_t n_tokens, double now, int32_t* slots_out,
+                    int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies);
+int tl_alloc_tables(const tl_page_allocator* a, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                    int32_t* tables, int32_t* lens);
+int tl_kv_copy_pages(const tl_kv_pool* pool, const int32_t* src_pages, const int32_t* dst_pages,
+                     int32_t n, void* stream);
 
 /*
  * Copy sequence positions 0..length-1 out of the pool in logical order, as stored

@@ -25,7 +25,7 @@ KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8u": 3, "int8": 4}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8u": 1, "int8": 1}
 SCALED = ("fp8", "int8")
 
-TL_OK, TL_ERR_INVALID, TL_ERR_UNSUPPORTED, TL_ERR_WORKSPACE, TL_ERR_HIP = 0, -1, -2, -3, -4
+TL_OK, TL_ERR_INVALID, TL_ERR_UNSUPPORTED, TL_ERR_WORKSPACE, TL_ERR_HIP, TL_ERR_NO_PAGES = 0, -1, -2, -3, -4, -5
 
 
 class TLError(RuntimeError):
@@ -66,6 +66,22 @@ def lib() -> ctypes.CDLL:
         L.tl_paged_attn_prefill_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
         L.tl_kv_gather.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
         L.tl_gated_delta_rule_decode.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        f64 = ctypes.c_double
+        L.tl_alloc_create.argtypes = [i32, i32, f64]
+        L.tl_alloc_create.restype = vp
+        L.tl_alloc_destroy.argtypes = [vp]
+        L.tl_alloc_destroy.restype = None
+        L.tl_alloc_free_pages.argtypes = [vp]
+        L.tl_alloc_free_pages.restype = i32
+        L.tl_alloc_start.argtypes = [vp, i64, f64]
+        L.tl_alloc_end.argtypes = [vp, i64]
+        L.tl_alloc_fork.argtypes = [vp, i64, i64, i64, f64]
+        L.tl_alloc_append.argtypes = [vp, i64, i32, f64, vp, vp, vp, vp]
+        L.tl_alloc_tables.argtypes = [vp, vp, i32, i32, vp, vp]
+        L.tl_kv_copy_pages.argtypes = [P, vp, vp, i32, vp]
+        for fn in ("tl_alloc_start", "tl_alloc_end", "tl_alloc_fork", "tl_alloc_append", "tl_alloc_tables",
+                   "tl_kv_copy_pages"):
+            getattr(L, fn).restype = ctypes.c_int
         L.tl_last_error.restype = ctypes.c_char_p
         L.tl_abi_version.restype = ctypes.c_int
         for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather",
@@ -272,6 +288,64 @@ def tl_gated_delta_rule_decode(state_pool, q, k, v, g, beta, state_slots, positi
                                             state_slots.data_ptr(), positions.data_ptr(), B, out.data_ptr(),
                                             _stream(stream)))
     return out
+
+
+class PageAllocator:
+    """The library's host page allocator (include/tl.h: tl_alloc_*), marshalled with
+    ctypes: per-sequence pages, refusal by name (TLError with code TL_ERR_NO_PAGES),
+    least-recently-active reclaim of idle sequences, and prefix sharing with
+    copy-on-write."""
+
+    def __init__(self, num_pages: int, page_size: int, idle_timeout: float):
+        self._h = lib().tl_alloc_create(num_pages, page_size, idle_timeout)
+        if not self._h:
+            raise TLError(TL_ERR_INVALID, lib().tl_last_error().decode())
+        self.page_size = page_size
+
+    def close(self) -> None:
+        if self._h:
+            lib().tl_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def free_pages(self) -> int:
+        return int(lib().tl_alloc_free_pages(self._h))
+
+    def start(self, seq: int, now: float) -> None:
+        _check(lib().tl_alloc_start(self._h, seq, now))
+
+    def end(self, seq: int) -> None:
+        _check(lib().tl_alloc_end(self._h, seq))
+
+    def fork(self, parent: int, child: int, n_tokens: int, now: float) -> None:
+        _check(lib().tl_alloc_fork(self._h, parent, child, n_tokens, now))
+
+    def append(self, seq: int, n_tokens: int, now: float):
+        """Slots of the next n_tokens positions and the page copies [(src, dst)] to run first."""
+        slots = (ctypes.c_int32 * max(n_tokens, 1))()
+        src, dst, nc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().tl_alloc_append(self._h, seq, n_tokens, now, slots, ctypes.byref(src), ctypes.byref(dst),
+                                     ctypes.byref(nc)))
+        return list(slots)[:n_tokens], [(src.value, dst.value)] if nc.value else []
+
+    def tables(self, seqs, max_blocks: int):
+        """Block tables [len(seqs)][max_blocks] (-1 unused) and lengths, as Python lists."""
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*seqs)
+        tab = (ctypes.c_int32 * max(n * max_blocks, 1))()
+        lens = (ctypes.c_int32 * max(n, 1))()
+        _check(lib().tl_alloc_tables(self._h, ids, n, max_blocks, tab, lens))
+        flat = list(tab)
+        return [flat[i * max_blocks:(i + 1) * max_blocks] for i in range(n)], list(lens)[:n]
+
+
+def tl_kv_copy_pages(pool: KVPool, src_pages, dst_pages, stream=None) -> None:
+    """Device copy of whole pages src_pages[i] -> dst_pages[i] (int32 device tensors)."""
+    ps = pool.c_struct()
+    _check(lib().tl_kv_copy_pages(ctypes.byref(ps), src_pages.data_ptr(), dst_pages.data_ptr(), int(src_pages.numel()),
+                                  _stream(stream)))
 
 
 def tl_kv_gather(pool: KVPool, block_table_row, length: int, stream=None):

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtl.so")
-SOURCES = ["tl_api.hip", "tl_write.hip", "tl_decode.hip", "tl_prefill.hip", "tl_gdn.hip"]
+SOURCES = ["tl_api.hip", "tl_write.hip", "tl_decode.hip", "tl_prefill.hip", "tl_gdn.hip", "tl_alloc.hip"]
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
 HIP_FLAGS = [

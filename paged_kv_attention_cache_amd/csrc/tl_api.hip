@@ -13,7 +13,7 @@
 
 namespace {
 
-thread_local char g_err[512] = "";
+thread_local char g_err[2048] = "";
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -275,6 +275,13 @@ int prefill_common(const char* fn, const tl_kv_pool* pool, const float* q, int32
 
 }  // namespace
 
+namespace tl {
+int set_error(int code, const char* msg) {
+  snprintf(g_err, sizeof(g_err), "%s", msg);
+  return code;
+}
+}  // namespace tl
+
 extern "C" {
 
 const char* tl_last_error(void) { return g_err; }
@@ -421,6 +428,30 @@ int tl_gated_delta_rule_decode(float* state_pool, int32_t num_slots, int32_t num
   a.slots = state_slots; a.positions = positions; a.out = out;
   a.batch = batch; a.num_heads = num_heads; a.num_slots = num_slots;
   hipError_t e = tl::launch_gdn_decode(a, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+int tl_kv_copy_pages(const tl_kv_pool* pool, const int32_t* src_pages, const int32_t* dst_pages, int32_t n,
+                     void* stream) {
+  const char* fn = "tl_kv_copy_pages";
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if (n < 0) return fail(TL_ERR_INVALID, "%s: n (%d) must be >= 0", fn, n);
+  if (n == 0) return ok();
+  if (n > 65535) return fail(TL_ERR_UNSUPPORTED, "%s: n (%d) must be <= 65535", fn, n);
+  if (!src_pages || !dst_pages) return fail(TL_ERR_INVALID, "%s: src_pages/dst_pages is NULL", fn);
+  if (!aligned(src_pages, 4) || !aligned(dst_pages, 4))
+    return fail(TL_ERR_INVALID, "%s: src_pages/dst_pages is not 4-byte aligned", fn);
+  tl::CopyPagesArgs a;
+  const int bytes = pool->dtype == TL_KV_F32 ? 4 : pool->dtype == TL_KV_BF16 ? 2 : 1;
+  const bool scaled = pool->dtype == TL_KV_FP8_E4M3 || pool->dtype == TL_KV_INT8;
+  a.k = pool->k; a.v = pool->v;
+  a.k_scale = scaled ? pool->k_scale : nullptr; a.v_scale = scaled ? pool->v_scale : nullptr;
+  a.num_pages = pool->num_pages;
+  a.units = (int64_t)pool->num_kv_heads * pool->page_size * pool->head_dim * bytes / 16;
+  a.scales = (int64_t)pool->num_kv_heads * pool->page_size;
+  hipError_t e = tl::launch_copy_pages(a, src_pages, dst_pages, n, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
 }

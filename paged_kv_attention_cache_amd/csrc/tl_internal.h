@@ -165,5 +165,14 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s);
 int prefill_tokens_per_wg(int group);
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t s);
 hipError_t launch_gdn_decode(const GdnArgs& a, hipStream_t s);
+struct CopyPagesArgs {
+  void *k, *v;
+  float *k_scale, *v_scale;  // NULL for unscaled pools
+  int num_pages;
+  int64_t units;   // 16-byte units of K (and of V) per page
+  int64_t scales;  // scales per page (num_kv_heads * page_size)
+};
+hipError_t launch_copy_pages(const CopyPagesArgs& p, const int32_t* src, const int32_t* dst, int n, hipStream_t s);
+int set_error(int code, const char* msg);  // the thread's tl_last_error() text; returns code
 
 }  // namespace tl
