@@ -37,9 +37,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("tl_decode.hip", "tl_prefill.hip", "tl_write.hip", "tl_gdn.hip", "tl_internal.h")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources of the measured kernels (the traffic record is valid while it matches)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_attention_cache_amd", "csrc"))):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_attention_cache_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -220,7 +224,7 @@ def cpu_baseline(target_s: float = 12.0, cap_s: float = 30.0):
 # These modes make no GPU call except --copy-calibration; they turn the CSV output of
 # rocprofv3 runs of this file into the short text summaries kept under profiles/.
 
-ATTN_KERNELS = ("decode_split_kernel", "decode_merge_kernel", "decode_prep_kernel", "prefill_kernel")
+ATTN_KERNELS = ("decode_split_kernel", "decode_merge_kernel", "prefill_kernel", "gdn_decode_kernel")
 
 
 def _short_name(name: str) -> str:
@@ -313,7 +317,8 @@ def stats_summary(d: str, configs: str, calls: str, command: str):
     rows = sorted(csv.DictReader(open(_find_csv(d, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"]))
     n = int(calls)
     att = [r for r in rows if any(k in r["Kernel_Name"] for k in ATTN_KERNELS)]
-    mains = [i for i, r in enumerate(att) if "decode_split_kernel" in r["Kernel_Name"] or "prefill_kernel" in r["Kernel_Name"]]
+    mains = [i for i, r in enumerate(att) if any(k in r["Kernel_Name"] for k in
+                                                 ("decode_split_kernel", "prefill_kernel", "gdn_decode_kernel"))]
     print(f"command: {command}\n")
     print("Durations from the kernel trace (rocprofv3 --kernel-trace --stats), grouped by workload.\n")
     print("| workload | kernel | calls | average us | min us | max us |")
@@ -373,7 +378,12 @@ def main():
         log(f"[bench] {n}: " + json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}))
 
     head_wl, head = results[names[0]]
-    if head["kind"] == "decode":
+    if head["kind"] == "gdn":  # (only when the state-pool workload is run first)
+        value, unit = head["attn_bytes"] / (head["ms_per_step"] * 1e-3) / 1e9, "GB/s"
+        roof = {"bound": "hbm", "achieved": head["attn_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": head["attn_GBps"] / HBM_PEAK_GBPS, "kernel": "gdn_decode_kernel",
+                "per_launch_bytes": head["attn_bytes"]}
+    elif head["kind"] == "decode":
         value, unit = head["step_GBps"], "GB/s"
         per_launch = head["attn_bytes"]
         roof = {"bound": "hbm", "achieved": head["attn_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -391,9 +401,12 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": head_wl.name, "batch": head_wl.batch, "num_q_heads": head_wl.num_q_heads,
-                   "num_kv_heads": head_wl.num_kv_heads, "head_dim": head_wl.head_dim,
-                   "page_size": head_wl.page_size, "kv_dtype": head_wl.kv_dtype, "parallelism": "none"},
+        "config": ({"workload": head_wl.name, "batch": head_wl.batch, "num_heads": head_wl.num_heads,
+                    "head_dim": head_wl.head_dim, "num_slots": head_wl.num_slots, "parallelism": "none"}
+                   if head["kind"] == "gdn" else
+                   {"workload": head_wl.name, "batch": head_wl.batch, "num_q_heads": head_wl.num_q_heads,
+                    "num_kv_heads": head_wl.num_kv_heads, "head_dim": head_wl.head_dim,
+                    "page_size": head_wl.page_size, "kv_dtype": head_wl.kv_dtype, "parallelism": "none"}),
         "roofline": roof,
     }
     line["secondary"] = {n: r for n, (_, r) in results.items() if n != names[0]}
