@@ -906,7 +906,18 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       VBuf<KVT, D> vA, vB_;
       VBuf<KVT, D>& vB = (PF >= 2) ? vB_ : vA;  // one V buffer unless V is prefetched
       int par = 0;
-      if (k0 <= k_end) {
+      if constexpr (PF == 0) {
+        // no buffer alternates: one copy of the tile in the loop, one peeled
+        if (k0 <= k_end) {
+          while (k0 + STEP <= k_end) {
+            decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l);
+            k0 += STEP;
+          }
+          decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, claim);
+        } else {
+          claim();
+        }
+      } else if (k0 <= k_end) {
         if constexpr (PF >= 1) load_k<KVT, D>(kA, a, sp, k0);
         if constexpr (PF >= 2) load_v<KVT, D>(vA, a, sp, k0);
         while (k0 + STEP <= k_end) {
@@ -916,8 +927,11 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
           decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l);
           k0 += STEP;
         }
-        if (par == 0) decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, claim);
-        else decode_tile<KVT, D, PF>(a, sp, kB, kA, vB, vA, k0, k0 + STEP, q, o, m, l, claim);
+        if (par) {  // the last tile's prefetched operands sit in the B buffers
+          kA = kB;
+          if constexpr (PF >= 2) vA = vB;
+        }
+        decode_tile<KVT, D, PF>(a, sp, kA, kB, vA, vB, k0, k0 + STEP, q, o, m, l, claim);
       } else {
         claim();
       }
