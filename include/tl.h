@@ -132,12 +132,14 @@ int tl_kv_cache_write(const tl_kv_pool* pool, const float* k_new, const float* v
  *   scale         multiplies q.k (e.g. 1/sqrt(head_dim))
  *   out           [batch][num_q_heads][head_dim] f32
  *   workspace     device scratch of at least tl_paged_attn_decode_workspace_size(...)
- *                 bytes: a work counter in its first 16 bytes (the same place for
- *                 every shape), then partial softmax states.  Those first 16 bytes
- *                 must be zero before its first use; every call leaves the counter
- *                 at zero again, so it can be reused by later calls of any shape on
- *                 the same stream without clearing.  Two calls in flight at once (on
- *                 different streams) need separate workspaces.
+ *                 bytes: a header of 524,304 bytes (16 bytes of work counters, then
+ *                 one arrival counter per (sequence, head group) that the in-place
+ *                 merge of the splits uses; the same bytes for every shape), then
+ *                 partial softmax states.  The header must be zero before the first
+ *                 use; every call leaves it at zero again, so the workspace can be
+ *                 reused by later calls of any shape on the same stream without
+ *                 clearing (the partial states need no initial value).  Two calls in
+ *                 flight at once (on different streams) need separate workspaces.
  * Query head h reads kv head h / (num_q_heads / num_kv_heads).
  * Results depend only on each sequence's own inputs (no cross-sequence reductions),
  * so a sequence's output is the same bits in any batch.

@@ -135,9 +135,9 @@ int64_t ring_nsplit(const tl_kv_pool* pool, int32_t num_q_heads, int32_t ring_pa
 }
 
 size_t decode_ws_bytes(const tl_kv_pool* pool, int32_t batch, int32_t num_q_heads, int64_t ns) {
-  // 16 bytes of control words (at offset 0 whatever the shape), then the partial
-  // states (acc, then m and l)
-  return 16 + (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float);
+  // the control words and arrival counters (the same bytes whatever the shape), then
+  // the partial states (acc, then m and l)
+  return (size_t)tl::DECODE_WS_HEADER + (size_t)batch * num_q_heads * ns * (pool->head_dim + 2) * sizeof(float);
 }
 
 // Shared by the full-table and ring decode entries.  ring = 0: block_tables has
@@ -195,13 +195,15 @@ int decode_common(const char* fn, const tl_kv_pool* pool, const float* q, int32_
   a.pool = pool_args(pool);
   a.q = q; a.block_tables = block_tables; a.seq_lens = seq_lens; a.out = out;
   a.ws_ctrl = reinterpret_cast<int*>(workspace);  // same place for every shape
-  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 16);
+  a.ws_arrive = reinterpret_cast<int*>(static_cast<char*>(workspace) + 16);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + tl::DECODE_WS_HEADER);
   a.ws_ml = a.ws_acc + (size_t)batch * num_q_heads * ns * pool->head_dim;
   a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = width;
   a.batch = batch; a.window = ring ? ring_window(pool, ring, window) : window;
   a.ring = ring;
   a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->page_size);
   a.n_split = (int)ns;
+  a.fuse_merge = 0;  // chosen per kernel at launch
   a.qscale = scale * tl::LOG2E;
   hipError_t e = tl::launch_decode(a, pool->dtype, s);
   if (e != hipSuccess) return hip_fail(fn, e);

@@ -25,6 +25,7 @@
 // - fp8: the per-(token, head) K scale multiplies the finished dot; the V scale
 //   multiplies the probability before the value product (the sum over keys is
 //   unchanged, since both are per key).
+#include <type_traits>
 #include <utility>
 
 #include "tl_internal.h"
@@ -727,6 +728,107 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
   }
 }
 
+// Partial states cross workgroups (and XCDs, whose L2 caches are not coherent with
+// each other) inside one launch when the splits merge in place.  They are then
+// written and read with device-scope relaxed atomics, which go to the coherent level
+// instead of a non-coherent cached copy; the writer waits for its stores to complete
+// before it counts its split, and the reader loads only after it has seen the count.
+// No cache-wide writeback or invalidate is needed (device-scope fences would cost
+// one on every split).
+template <bool COH>
+__device__ __forceinline__ void store1(float* p, float v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void store2(float* p, float x, float y) {
+  if constexpr (!COH) {
+    *reinterpret_cast<float2*>(p) = make_float2(x, y);
+    return;
+  }
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool COH>
+__device__ __forceinline__ float2 load2(const float* p) {
+  if constexpr (!COH) return *reinterpret_cast<const float2*>(p);
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Merge of the splits s_base .. s_base + ns - 1 of q heads hq0 .. hq0 + nh - 1 of
+// sequence b (nh <= 8) by one workgroup of NTHR threads, from partial states that
+// other workgroups of the same launch stored: m* = max m_s, then
+// o = sum 2^(m_s - m*) acc_s / sum 2^(m_s - m*) l_s (log2 units), the sums taken in
+// split order.  Thread t takes head t / (NTHR / 8) and VPT consecutive values of it;
+// up to MB splits are loaded in one batch, so a sequence of at most MB splits waits
+// for one round of loads.
+template <int D, int NTHR>
+__device__ __forceinline__ void merge_group(const DecodeArgs& a, int b, int hq0, int nh, int s_base, int ns, int tid) {
+  constexpr int TPH = NTHR / 8, VPT = D / TPH, NP = VPT / 2, MB = 16;
+  static_assert(VPT == 2 || VPT == 4 || VPT == 8, "values per thread");
+  const int h = tid / TPH, d0 = (tid % TPH) * VPT;
+  if (h >= nh) return;
+  const int64_t bh = (int64_t)b * a.num_q_heads + hq0 + h;
+  const float* ml = a.ws_ml + (bh * a.n_split + s_base) * 2;
+  const float* acc = a.ws_acc + (bh * a.n_split + s_base) * D + d0;
+  float o[VPT] = {};
+  float l = 0.0f, mstar = -INFINITY;
+  auto add = [&](float wgt, const float2 (&v)[NP]) {
+#pragma unroll
+    for (int n = 0; n < NP; ++n) { o[2 * n] += wgt * v[n].x; o[2 * n + 1] += wgt * v[n].y; }
+  };
+  for (int s0 = 0; s0 < ns; s0 += MB) {  // m* first (one pass when ns <= MB: the loads are shared)
+    if (ns <= MB) break;
+    float2 x[MB];
+#pragma unroll
+    for (int u = 0; u < MB; ++u) x[u] = load2<true>(ml + 2 * min(s0 + u, ns - 1));
+#pragma unroll
+    for (int u = 0; u < MB; ++u)
+      if (s0 + u < ns) mstar = fmaxf(mstar, x[u].x);
+  }
+  for (int s0 = 0; s0 < ns; s0 += MB) {
+    float2 x[MB], av[MB][NP];
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int sx = min(s0 + u, ns - 1);
+      x[u] = load2<true>(ml + 2 * sx);
+#pragma unroll
+      for (int n = 0; n < NP; ++n) av[u][n] = load2<true>(acc + (int64_t)sx * D + 2 * n);
+    }
+    if (ns <= MB) {
+#pragma unroll
+      for (int u = 0; u < MB; ++u)
+        if (u < ns) mstar = fmaxf(mstar, x[u].x);
+    }
+    const float mu = mstar == -INFINITY ? 0.0f : mstar;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      if (s0 + u < ns) {
+        const float wgt = fast_exp2(x[u].x - mu);
+        l += wgt * x[u].y;
+        add(wgt, av[u]);
+      }
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* dst = a.out + bh * D + d0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) dst[i] = l > 0.0f ? o[i] * inv : 0.0f;
+}
+
+// The workgroup that finishes last resets the item and finished-workgroup counters
+// for the next call.  A workgroup's last claim has returned before it arrives here, so
+// no claim can follow the reset.
+__device__ __forceinline__ void workgroup_done(const DecodeArgs& a, int tid) {
+  if (tid == 0) {
+    if (atomicAdd(a.ws_ctrl + 1, 1) == (int)gridDim.x - 1) {
+      __hip_atomic_store(a.ws_ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ws_ctrl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Persistent workgroups of NWD waves.  For each claimed item, wave w takes the
 // split's tiles w, w + NWD, ... with its own softmax state; the NWD states are then
 // combined through LDS in wave order, so the result depends on the split alone, not
@@ -743,6 +845,9 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   constexpr int NT = GE::NT;
   constexpr int PF = DecodePrefetch<KVT, D, G>::value;
   constexpr int STEP = NWD * TK;
+  // In-place merge on the exact-split path only (measured: it saves the merge launch
+  // there, while the register-tile kernels lose more than that to it)
+  constexpr bool FUSE = XP;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int slot = lane >> 5, kg = (lane >> 2) & 7, j = lane & 3;
   const int H = a.pool.num_kv_heads;
@@ -754,7 +859,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   tabs.full = dyn + a.batch;
 #pragma unroll
   for (int k = 0; k < NBKT; ++k) tabs.bkt[k] = dyn + (2 + k) * a.batch;
-  __shared__ int c_carry[1 + NBKT], c_wsum[NWD][1 + NBKT], s_claim[1];
+  __shared__ int c_carry[1 + NBKT], c_wsum[NWD][1 + NBKT], s_claim[1], s_last[1];
   __shared__ float c_acc[NWD][NT * 4][64];    // [wave][value i*4 + r][lane]
   __shared__ float c_m[NWD][8], c_l[NWD][8];  // [wave][slot*4 + head]
   __shared__ bf16x8 x_q[XP ? 8 * 64 : 1];  // exact-split path: Q3 operands of the item
@@ -812,14 +917,48 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
 #pragma unroll
   for (int k = 0; k < NBKT; ++k) n_pairs += tabs.bkt[k][a.batch - 1];
   const int n_items = uni(n_pairs * gy);
+  if (FUSE && a.fuse_merge) {
+    // rows of empty sequences are zero (they have no items); workgroup i takes
+    // sequences i, i + n_wg, ...
+    for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+      if (tabs.len[b] > 0) continue;
+      float* o = a.out + (int64_t)b * a.num_q_heads * D;
+      for (int i = tid; i < a.num_q_heads * D; i += NTHR) o[i] = 0.0f;
+    }
+  }
   // the first item of each workgroup is fixed; later ones come from the counter
   const int n_wg = gridDim.x;
   int cur = blockIdx.x;
-  if (cur >= n_items) return;  // workgroup-uniform
+  if (cur >= n_items) {  // workgroup-uniform
+    if constexpr (FUSE) workgroup_done(a, tid);
+    return;
+  }
   Item it = item_of<RING>(a, tabs, cur, gy);
   ItemOps<XP ? 8 : D / 8> op;
   item_ops<D, G, XP, RING>(a, it, lane, w, op);
   if constexpr (XP) xqueries(op.q, a.qscale, lane, w, x_q);  // scores come out in log2 units
+
+  // In-place merge.  A split's partial states are counted one item later, when the
+  // workgroup's next item reaches its combine: by then the coherent stores have long
+  // completed, so the wait before the count costs nothing.  The workgroup whose count
+  // completes a (sequence, head group) merges it.  pend_b < 0: nothing to count.
+  int pend_b = -1, pend_y = 0, pend_ns = 0, pend_base = 0;
+  auto count_pending = [&]() {  // after a barrier that follows every wave's wait
+    int* arrive = a.ws_arrive + (int64_t)pend_b * gy + pend_y;
+    if (tid == 0) s_last[0] = atomicAdd(arrive, 1) == pend_ns - 1;
+    __syncthreads();
+    if (s_last[0]) {
+      int hq0, nh;
+      if constexpr (G == 8) {
+        hq0 = pend_y * 8; nh = 8;
+      } else {
+        hq0 = pend_y * 2 * G; nh = (pend_y * 2 + 1 < H) ? 2 * G : G;
+      }
+      merge_group<D, NTHR>(a, pend_b, hq0, nh, pend_base, pend_ns, tid);
+      if (tid == 0) __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+    }
+    pend_b = -1;
+  };
 
   for (;;) {
     __syncthreads();  // the previous item's combine is done everywhere
@@ -945,6 +1084,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
         for (int r = 0; r < 4; ++r) c_acc[w][i * 4 + r][lane] = o[i][r];
       if (kg == 0) { c_m[w][slot * 4 + j] = m; c_l[w][slot * 4 + j] = l; }
     }
+    if (FUSE && pend_b >= 0) __builtin_amdgcn_s_waitcnt(0);  // the previous item's partial stores have completed
     if (tid == 0) s_claim[0] = claimed;
     __syncthreads();
     // the next item's table entries and queries load while this one is combined
@@ -958,6 +1098,9 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     if (has_next) {
       nit = item_of<RING>(a, tabs, nxt, gy);
       item_ops<D, G, XP, RING>(a, nit, lane, w, nop);
+    }
+    if constexpr (FUSE) {
+      if (pend_b >= 0) count_pending();
     }
 
     // ---- combine in wave order: value v = i*4 + r of this lane is head slot*4 + r,
@@ -987,12 +1130,13 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       } else {
         // a ring row's splits are stored from its first (their numbers grow without end)
         const int rs = RING ? it.split - ss.s_first : it.split;
-        a.ws_acc[(((int64_t)it.b * a.num_q_heads + hq) * a.n_split + rs) * D + d] = acc;
-        if (i == 0 && (lane & 31) == 0) {
-          float* dst = a.ws_ml + (((int64_t)it.b * a.num_q_heads + hq) * a.n_split + rs) * 2;
-          *reinterpret_cast<float2*>(dst) = make_float2(ms, lsum);
-        }
+        store1<FUSE>(a.ws_acc + (((int64_t)it.b * a.num_q_heads + hq) * a.n_split + rs) * D + d, acc);
+        if (i == 0 && (lane & 31) == 0)
+          store2<FUSE>(a.ws_ml + (((int64_t)it.b * a.num_q_heads + hq) * a.n_split + rs) * 2, ms, lsum);
       }
+    }
+    if (FUSE && !single && a.fuse_merge) {
+      pend_b = it.b; pend_y = it.y; pend_ns = ss.s_last - ss.s_first + 1; pend_base = RING ? 0 : ss.s_first;
     }
     if (!has_next) break;  // workgroup-uniform
     // (exact-split path: every wave is past the barrier above, so no tile reads the
@@ -1000,6 +1144,14 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     if constexpr (XP) xqueries(nop.q, a.qscale, lane, w, x_q);
     it = nit;
     op = nop;
+  }
+  if constexpr (FUSE) {
+    if (pend_b >= 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      count_pending();
+    }
+    workgroup_done(a, tid);
   }
 }
 
@@ -1098,7 +1250,13 @@ hipError_t decode_launch_split_r(const DecodeArgs& a, hipStream_t s) {
   const int64_t upper = (int64_t)a.batch * a.n_split * gy;
   constexpr int threads = 64 * DecodeWaves<XP>::value;
   const int64_t wgs = std::min<int64_t>(upper, resident_workgroups<decode_split_kernel<KVT, D, G, XP, RING>>(threads, dyn));
-  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP, RING>), dim3((unsigned)wgs), dim3(threads), dyn, s, a);
+  DecodeArgs c = a;
+  // in place on the exact-split path when the arrival counters cover every head group
+  c.fuse_merge = XP && gy <= DECODE_ARRIVE_GROUPS;
+  hipLaunchKernelGGL((decode_split_kernel<KVT, D, G, XP, RING>), dim3((unsigned)wgs), dim3(threads), dyn, s, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c.fuse_merge) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.batch * a.num_q_heads)), dim3(64), 0, s, c);
   return hipGetLastError();
 }
 
@@ -1127,9 +1285,7 @@ hipError_t decode_dispatch_g(const DecodeArgs& a, hipStream_t s) {
     case 2: e = decode_launch_split<KVT, D, 2>(a, s); break;
     default: e = decode_launch_split<KVT, D, 1>(a, s); break;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.num_q_heads), dim3(64), 0, s, a);
-  return hipGetLastError();
+  return e;
 }
 
 template <int KVT>
@@ -1153,9 +1309,10 @@ int decode_split_keys(int kv_dtype, int group, int page_size) {
 }
 
 // Batches larger than DECODE_BATCH_CHUNK run as consecutive launches over slices of
-// the batch (the per-workgroup item tables hold 12 bytes of LDS per sequence).
+// the batch (the per-workgroup item tables hold 24 bytes of LDS per sequence).
 // Sequences are independent, so a slice computes exactly what the whole batch would.
-constexpr int DECODE_BATCH_CHUNK = 2048;
+// The exact-split kernel merges its splits in place when the arrival counters cover
+// every head group; otherwise a merge kernel follows the split kernel.
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s) {
   for (int b0 = 0; b0 < a.batch; b0 += DECODE_BATCH_CHUNK) {

@@ -129,11 +129,21 @@ struct DecodeArgs {
   float* out;
   float* ws_acc;   // [batch][num_q_heads][n_split][head_dim], split index from the row's first
   float* ws_ml;    // [batch][num_q_heads][n_split][2]
-  int* ws_ctrl;    // [4]: the item counter (zero between calls)
+  int* ws_ctrl;    // [4]: the item counter, the finished-workgroup counter (zero between calls)
+  int* ws_arrive;  // [DECODE_ARRIVE_SLOTS]: splits stored per (sequence, head group) (zero between calls)
+  int fuse_merge;  // 1: the last split of a (sequence, head group) merges; 0: a merge kernel follows
   int num_q_heads, group, max_blocks, batch, window, split_keys, n_split;
   int ring;        // 0: block j of a sequence is block_tables entry j; R > 0: entry j % R
   float qscale;    // scale * log2(e): scores come out in log2 units
 };
+
+// Decode workspace: 16 bytes of control words, then the arrival counters of the
+// in-place merge (a fixed count, so no later call's counters overlap an earlier
+// call's partial states), then the partial states.
+constexpr int DECODE_BATCH_CHUNK = 2048;  // sequences per launch
+constexpr int DECODE_ARRIVE_GROUPS = 64;  // head groups per sequence the counters cover
+constexpr int64_t DECODE_ARRIVE_SLOTS = (int64_t)DECODE_BATCH_CHUNK * DECODE_ARRIVE_GROUPS;
+constexpr int64_t DECODE_WS_HEADER = 16 + DECODE_ARRIVE_SLOTS * 4;
 
 struct PrefillArgs {
   PoolArgs pool;

@@ -92,14 +92,19 @@ def test_decode_rejects_bad_arguments():
     assert _decode(p, batch=0) == tl.TL_OK
 
 
+# control words, then one arrival counter per (sequence of a 2048-sequence launch, head
+# group of up to 64), at the same place for every shape
+WS_HEADER = 16 + 2048 * 64 * 4
+
+
 def test_decode_workspace_size_formula():
     p = _pool(dtype=1, page_size=16, head_dim=128)
     # bf16 splits are 512 keys (32 pages of 16): 128 blocks of 16 = 2048 keys -> 4 splits
     n = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p), 3, 8, 128)
-    assert n == 3 * 8 * 4 * (128 + 2) * 4 + 16  # partial states (acc + m, l) and 16 control bytes
+    assert n == 3 * 8 * 4 * (128 + 2) * 4 + WS_HEADER  # partial states (acc + m, l) after the header
     p8 = _pool(dtype=2, page_size=64, head_dim=128)
     n8 = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p8), 2, 16, 512)  # 32768 keys / 4096
-    assert n8 == 2 * 16 * 8 * 130 * 4 + 16
+    assert n8 == 2 * 16 * 8 * 130 * 4 + WS_HEADER
     assert tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p), 3, 7, 64) == 0
 
 
@@ -148,11 +153,11 @@ def test_ring_entries_reject_bad_arguments_and_size_their_workspace():
     assert rc == tl.TL_ERR_INVALID and "ring_tables" in tl.tl_last_error()
     # ring of 8 pages of 16 = 128 slots; window 100 spans at most 99 // 512 + 2 = 2 splits of 512 keys
     n = L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 3, 8, 8, 100)
-    assert n == 16 + 3 * 8 * 2 * (128 + 2) * 4
+    assert n == WS_HEADER + 3 * 8 * 2 * (128 + 2) * 4
     # no window: the ring's 128 slots
     assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 3, 8, 8, 0) == n
     # a window wider than a large ring is cut to the ring: 4096 slots -> 4095 // 512 + 2 = 9 splits
-    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 1, 8, 256, 10 ** 6) == 16 + 8 * 9 * 130 * 4
+    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 1, 8, 256, 10 ** 6) == WS_HEADER + 8 * 9 * 130 * 4
     rc = L.tl_paged_attn_decode_ring(ctypes.byref(p), 0x8000, 8, 0xA000, 8, 0xB000, 3, 100, f, 0xC000, 0x9000, n - 1,
                                      None)
     assert rc == tl.TL_ERR_WORKSPACE

@@ -172,6 +172,10 @@ DECODE_CASES = [
     ("g4_int8", [1, 513, 3000], 8, 2, 128, 16, "int8", 0),
     ("g8_int8_window", [4097, 900], 16, 2, 128, 64, "int8", 1000),
     ("g1_int8_d64", [70, 5], 4, 4, 64, 16, "int8", 0),
+    # exact-split path with 64 head groups: the most its in-place merge covers
+    ("g8_fp8_64_groups", [5000, 0, 9000], 512, 64, 128, 64, "fp8", 0),
+    # and with 65: a merge kernel follows the split kernel
+    ("g8_fp8_65_groups", [0, 4500, 9000, 1], 520, 65, 128, 64, "fp8", 0),
 ]
 
 
@@ -225,9 +229,28 @@ def test_decode_batch_invariance_bitwise(torch_cuda):
         assert torch.equal(one[0], full[b]), f"sequence {b} differs alone vs in batch"
 
 
+def test_decode_batch_over_one_launch(torch_cuda):
+    """2,100 sequences on the exact-split path run as two launches (2,048 + 52) that
+    share the workspace's counters; every row matches the oracle and empty rows are
+    zero."""
+    torch = torch_cuda
+    lens = np.random.default_rng(435).integers(0, 300, 2100)
+    lens[[0, 5, 2047, 2048, 2060, 2099]] = [0, 9000, 4097, 0, 8200, 4500]
+    wl = W.custom_decode(435, lens, 8, 1, 128, 64, "fp8")
+    op = oracle_pool_for(wl)
+    gp = R.make_pool(wl)
+    R.write_history(gp, wl)
+    st = R.DecodeStep(wl, gp)
+    got = st.run().cpu().numpy()
+    ref = oracle.decode(op, wl.decode_q(), wl.block_tables, wl.seq_lens, 0, wl.scale)
+    assert row_rel_err(got, ref) <= TOL["fp8"]
+    assert np.all(got[lens == 0] == 0)
+
+
 def test_decode_workspace_reused_across_calls(torch_cuda):
-    """One zero-filled workspace serves later calls of other shapes: each call leaves its
-    work counter at zero, and every result equals the one from a fresh workspace."""
+    """One workspace whose header is zero serves later calls of other shapes: each call
+    leaves the header (work counters and arrival counters) at zero, whatever the rest
+    of the workspace held, and every result equals the one from a fresh workspace."""
     torch = torch_cuda
     import paged_kv_attention_cache_amd as tl
     cases = [W.custom_decode(440, [1500, 77, 3000, 515], 16, 2, 128, 16, "bf16"),
@@ -242,7 +265,9 @@ def test_decode_workspace_reused_across_calls(torch_cuda):
         steps.append((wl, gp, st))
     need = max(tl.tl_paged_attn_decode_workspace_size(gp, wl.batch, wl.num_q_heads, wl.max_blocks)
                for wl, gp, _ in steps)
-    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    header = 16 + 2048 * 64 * 4
+    shared = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")  # partial-state bytes: any value
+    shared[:header] = 0
     fresh = []
     for wl, gp, st in steps:
         fresh.append(tl.tl_paged_attn_decode(gp, st.q, st.tables, st.seq_lens, wl.window, wl.scale).clone())
@@ -251,8 +276,8 @@ def test_decode_workspace_reused_across_calls(torch_cuda):
             out = tl.tl_paged_attn_decode(gp, st.q, st.tables, st.seq_lens, wl.window, wl.scale, workspace=shared)
             torch.cuda.synchronize()
             assert torch.equal(out, fresh[i]), f"case {i} round {rnd}: reused workspace changes the result"
-            ctrl = shared[0:4].cpu().numpy().view(np.int32)[0]
-            assert ctrl == 0, f"work counter left at {ctrl}"
+            hdr = shared[:header].cpu().numpy().view(np.int32)
+            assert not hdr.any(), f"header words left non-zero at {np.nonzero(hdr)[0][:8]}"
 
 
 # ===================================================================== prefill
