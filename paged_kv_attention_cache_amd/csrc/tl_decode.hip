@@ -1182,6 +1182,38 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int base = a.ring > 0 ? 0 : s0;  // ring rows store their splits from the first
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (int64_t)bh * a.n_split + base;
   const float* acc = a.ws_acc + ((int64_t)bh * a.n_split + base) * D + lane * PER;
+  if (ns <= 16) {
+    // every load at once (one round of latency), then the same sums in the same order
+    const float2 x = lane < ns ? ml[lane] : make_float2(-INFINITY, 0.0f);
+    float av[16][PER];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int s = min(u, ns - 1);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) av[u][i] = acc[(int64_t)s * D + i];
+    }
+    float mx = x.x;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = wave_xor_max(mx, m);
+    if (mx == -INFINITY) mx = 0.0f;
+    const float w = lane < ns ? fast_exp2(x.x - mx) : 0.0f;
+    float ls = w * x.y;
+    float o[PER] = {};
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u < ns) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += wu * av[u][i];
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ls = wave_xor_sum(ls, m);
+    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dst[i] = ls > 0.0f ? o[i] * inv : 0.0f;
+    return;
+  }
   float mstar = -INFINITY;
   for (int c = lane; c < ns; c += 64) mstar = fmaxf(mstar, ml[c].x);
 #pragma unroll
