@@ -142,9 +142,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillArgs a) {
   // (and the pad-only tiles, which return at once) fill the end.
   const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
   const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-  const int tile = nx - 1 - lin / (ny * nz);
+  const int step = lin / (ny * nz);
+  const int tile = nx - 1 - step;
   const int h = lin % ny;
+#ifdef TL_PREFILL_NO_ROTATE
   const int b = (lin / ny) % nz;
+#else
+  const int b = (lin / ny + step) % nz;  // rows rotate from one tile step to the next
+#endif
 
   const int T = a.tokens_per_row;
   const int tok = tile * TPG + w * TPW + col / G;
