@@ -139,17 +139,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillArgs a) {
   // right-aligned, so a later tile holds later positions and sees more keys).  The
   // dispatcher hands out launch ids in order, round-robin over the XCDs, so the heavy
   // tiles of every row start first and spread over the whole chip; the light ones
-  // (and the pad-only tiles, which return at once) fill the end.
+  // (and the pad-only tiles, which return at once) fill the end.  Within a tile step
+  // the rows rotate from one step to the next: the hand-out below the XCD level also
+  // follows the launch id, and without the rotation each of its partitions would get
+  // the same rows at every step, so the one holding the longest rows would set the time.
   const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
   const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
   const int step = lin / (ny * nz);
   const int tile = nx - 1 - step;
   const int h = lin % ny;
-#ifdef TL_PREFILL_NO_ROTATE
-  const int b = (lin / ny) % nz;
-#else
-  const int b = (lin / ny + step) % nz;  // rows rotate from one tile step to the next
-#endif
+  const int b = (lin / ny + step) % nz;
 
   const int T = a.tokens_per_row;
   const int tok = tile * TPG + w * TPW + col / G;
