@@ -58,9 +58,6 @@ __device__ __forceinline__ int page_of_lane(int tab, int local) {
 }
 __device__ __forceinline__ int page_uniform(int tab, int local) { return __builtin_amdgcn_readlane(tab, local); }
 
-#ifndef TL_DECODE_PREFETCH_BF16
-#define TL_DECODE_PREFETCH_BF16 0
-#endif
 // How far ahead a wave loads: 0 = each tile loads its own K and V; 1 = the next
 // tile's K is loaded with this tile's V; 2 = the next tile's K and V are loaded while
 // this tile computes.  Chosen by what fits in the register budget (1-byte tiles are
