@@ -14,4 +14,4 @@ invariants the pages state, and the pages' printed byte counts).
 """
 from . import alloc, encode, gdn, paged  # noqa: F401
 from .paged import (KVPool, KEY_BLOCK, attend_rows, attend_rows_blockwise, decode, decode_ring,  # noqa: F401
-                    prefill, prefill_ring, ring_slots)
+                    prefill, prefill_ring, ring_slots, slot_mapping)

@@ -122,6 +122,15 @@ class KVPool:
         k, v, ks, vs = self.gather_raw(table_row, length)
         return (enc.kv_values(k, ks, self.kv_dtype), enc.kv_values(v, vs, self.kv_dtype))
 
+    def copy_pages(self, src, dst) -> None:
+        """Copy whole pages src[i] -> dst[i] (K, V and scales), in order."""
+        for a, b in zip(src, dst):
+            self.k[b] = self.k[a]
+            self.v[b] = self.v[a]
+            if self.k_scale is not None:
+                self.k_scale[b] = self.k_scale[a]
+                self.v_scale[b] = self.v_scale[a]
+
     def pool_bytes(self) -> bytes:
         """The whole pool (K, V, then scales) as bytes, for byte-exact comparison."""
         parts = [self.k.tobytes(), self.v.tobytes()]
@@ -351,6 +360,36 @@ def ring_slots(ring_row: np.ndarray, positions: np.ndarray, page_size: int) -> n
     blk = np.where(p < 0, 0, p) // page_size
     slot = ring_row[blk % R] * page_size + np.where(p < 0, 0, p) % page_size
     return np.where(p < 0, -1, slot).astype(np.int32)
+
+
+def slot_mapping(tables: np.ndarray, positions: np.ndarray, page_size: int, num_pages: int,
+                 ring_pages: int = 0) -> np.ndarray:
+    """SLOT_MAPPING (ring_pages = 0) or WINDOW_SLOT_MAPPING (ring_pages = R) of a call.
+
+    tables [B, width], positions [B, T].  Position p of row b is on the page of its
+    block j = p // S (on a ring, j = (p // S) % R) at offset p % S, so its slot is
+    tables[b][j] * S + p % S.  A pad (p < 0), a block past the table and an entry
+    that is not a page of the pool give -1 (nothing is written there).
+    """
+    tables = np.asarray(tables, dtype=np.int64)
+    positions = np.asarray(positions, dtype=np.int64)
+    B, T = positions.shape
+    width = tables.shape[1]
+    out = np.full((B, T), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            p = int(positions[b, t])
+            if p < 0:
+                continue
+            j = p // page_size
+            if ring_pages > 0:
+                j %= ring_pages
+            if j >= width:
+                continue
+            page = int(tables[b, j])
+            if 0 <= page < num_pages:
+                out[b, t] = page * page_size + p % page_size
+    return out
 
 
 def ring_live_slots(L: int, window: int, n_slots: int) -> list[int]:
