@@ -57,9 +57,14 @@ struct Staged {
   float vs[PrefillCfg<KVT, D>::UPT];
 };
 
+// Keys are clamped into [key_lo, key_hi], the range some token of the workgroup can
+// see: a tile's keys outside it (before a window's first key, past the last position)
+// would read rows the caller never had to write, and although their probability is
+// exactly 0, 0 times a non-finite stored value is NaN in the value product.  A clamped
+// key re-reads a row inside the range, which is written and finite.
 template <int KVT, int D>
 __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs& a, const int32_t* table,
-                                           int h, int kt0, int key_hi, int tid) {
+                                           int h, int kt0, int key_lo, int key_hi, int tid) {
   using C = PrefillCfg<KVT, D>;
   const int S = a.pool.page_size, sh = a.pool.page_shift, H = a.pool.num_kv_heads;
 #pragma unroll
@@ -69,7 +74,7 @@ __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs
       // K unit u: key u % KT, chunk u / KT  (chunked K layout: keys of a chunk contiguous)
       {
         const int kk = u % KT, c = u / KT;
-        const int key = min(kt0 + kk, key_hi);
+        const int key = clampi(kt0 + kk, key_lo, key_hi);
         const int page = clampi(table[ring_entry(a, key >> sh)], 0, a.pool.num_pages - 1);
         const uint4* p = reinterpret_cast<const uint4*>(a.pool.k);
         st.k[i] = p[(((int64_t)page * H + h) * C::NC + c) * S + (key & (S - 1))];
@@ -78,7 +83,7 @@ __device__ __forceinline__ void stage_load(Staged<KVT, D>& st, const PrefillArgs
       // V unit u: key u / NC, part u % NC (row-major V)
       {
         const int kk = u / C::NC, c = u % C::NC;
-        const int key = min(kt0 + kk, key_hi);
+        const int key = clampi(kt0 + kk, key_lo, key_hi);
         const int page = clampi(table[ring_entry(a, key >> sh)], 0, a.pool.num_pages - 1);
         const uint4* p = reinterpret_cast<const uint4*>(a.pool.v);
         st.v[i] = p[(((int64_t)page * H + h) * S + (key & (S - 1))) * C::NC + c];
@@ -199,14 +204,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillArgs a) {
 
   const int t_first = klo / KT, t_last = khi / KT;
   Staged<KVT, D> st;
-  stage_load<KVT, D>(st, a, table, h, t_first * KT, khi, tid);
+  stage_load<KVT, D>(st, a, table, h, t_first * KT, klo, khi, tid);
   stage_store<KVT, D>(st, lds[0][0], lds[0][1], tid);
   __syncthreads();
 
   for (int t = t_first; t <= t_last; ++t) {
     const int buf = (t - t_first) & 1;
     const bool more = t < t_last;
-    if (more) stage_load<KVT, D>(st, a, table, h, (t + 1) * KT, khi, tid);
+    if (more) stage_load<KVT, D>(st, a, table, h, (t + 1) * KT, klo, khi, tid);
     const int kt0 = t * KT;
     if (kt0 <= w_hi && kt0 + KT - 1 >= w_lo) {
       const float* kl = lds[buf][0];
