@@ -161,7 +161,10 @@ int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_h
  *   q             [batch][tokens_per_row][num_q_heads][head_dim] f32
  *   positions     [batch][tokens_per_row] int32; -1 = pad (its output row is 0).
  *                 Every position's K/V (and all earlier visible ones) must already be
- *                 written, i.e. call tl_kv_cache_write for the chunk first.
+ *                 written, i.e. call tl_kv_cache_write for the chunk first.  Keys a
+ *                 row's tokens cannot see (before a window, past the last position)
+ *                 are never read; keys between the first one a row can see and the
+ *                 row's last position must hold written (finite) K/V.
  *   out           [batch][tokens_per_row][num_q_heads][head_dim] f32 (every row written)
  *   workspace     may be NULL when tl_paged_attn_prefill_workspace_size(...) is 0
  */
@@ -209,6 +212,29 @@ int tl_paged_attn_prefill_ring(const tl_kv_pool* pool, const float* q, int32_t n
                                const int32_t* positions, int32_t batch, int32_t tokens_per_row,
                                int32_t window, float scale, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * SLOT_MAPPING and WINDOW_SLOT_MAPPING ("How serving works in Tlaloc", section 3: the
+ * slot each new token's K/V is written at, an input of every entry beside the block
+ * tables; with a windowed pool, logical block j of a sequence is on its ring's page
+ * j % ringPages, so position p is written over position p - ringPages * page_size).
+ * Fills the slots that tl_kv_cache_write takes, for a whole call:
+ *   slots[b][t] = tables[b][j] * page_size + p % page_size,  p = positions[b][t],
+ *                 j = p / page_size            (ring_pages == 0: block tables)
+ *                 j = (p / page_size) % ring_pages   (ring_pages > 0: rings)
+ * and -1 where p < 0 (a pad), where j >= width, or where the entry is not a page of
+ * the pool ([0, num_pages)), so that the write skips those tokens.
+ *   tables     [batch][width] int32 (device): block tables or ring tables; a ring
+ *              occupies the first ring_pages entries of its row (ring_pages <= width)
+ *   positions  [batch][tokens_per_row] int32 (device)
+ *   slots      [batch][tokens_per_row] int32 (device, output)
+ *   page_size  a power of two in [8, 1024]; num_pages * page_size < 2^31
+ * With TL_VALIDATE=1, a live position past the table or naming an entry outside the
+ * pool is an error instead (nothing enqueued).
+ */
+int tl_slot_mapping(const int32_t* tables, int32_t width, int32_t ring_pages, const int32_t* positions,
+                    int32_t batch, int32_t tokens_per_row, int32_t page_size, int32_t num_pages, int32_t* slots,
+                    void* stream);
 
 /*
  * GATED_DELTA_RULE, decode step ("How serving works in Tlaloc", "Linear-attention

@@ -5,9 +5,10 @@ marshals arguments: every step of the path runs in the HIP kernels.  torch is
 used for device memory and streams.  The binding has no fallback: if the
 library is missing or its call fails, it raises.
 
-Names follow the C ABI: ``tl_kv_cache_write``, ``tl_paged_attn_decode``,
-``tl_paged_attn_prefill``, their ring forms ``tl_paged_attn_decode_ring`` and
-``tl_paged_attn_prefill_ring``, ``tl_kv_gather`` and the workspace-size queries.
+Names follow the C ABI: ``tl_kv_cache_write``, ``tl_slot_mapping``,
+``tl_paged_attn_decode``, ``tl_paged_attn_prefill``, their ring forms
+``tl_paged_attn_decode_ring`` and ``tl_paged_attn_prefill_ring``, ``tl_kv_gather``
+and the workspace-size queries.
 """
 from __future__ import annotations
 
@@ -17,8 +18,7 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# TL_LIBRARY may point at another build of the same ABI (e.g. a tuning variant)
-LIB_PATH = os.environ.get("TL_LIBRARY") or os.path.join(HERE, "libtl.so")
+LIB_PATH = os.path.join(HERE, "libtl.so")
 
 # fp8 and int8: one f32 scale per (token, kv head); fp8u: the unscaled fp8 pool
 KV_DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8u": 3, "int8": 4}
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.tl_paged_attn_decode_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp, sz, vp]
         L.tl_paged_attn_prefill_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
         L.tl_kv_gather.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
+        L.tl_slot_mapping.argtypes = [vp, i32, i32, vp, i32, i32, i32, i32, vp, vp]
         L.tl_gated_delta_rule_decode.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         f64 = ctypes.c_double
         L.tl_alloc_create.argtypes = [i32, i32, f64]
@@ -84,7 +85,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, fn).restype = ctypes.c_int
         L.tl_last_error.restype = ctypes.c_char_p
         L.tl_abi_version.restype = ctypes.c_int
-        for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather",
+        for fn in ("tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill", "tl_kv_gather", "tl_slot_mapping",
                    "tl_paged_attn_decode_ring", "tl_paged_attn_prefill_ring", "tl_gated_delta_rule_decode"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -264,16 +265,21 @@ def tl_paged_attn_prefill_ring(pool: KVPool, q, ring_tables, positions, window: 
     return out
 
 
-def ring_slot_mapping(ring_row, positions, page_size: int):
-    """Windowed slot mapping of a sequence's ring (host helper, numpy): position p is on
-    ring page ring_row[(p // page_size) % len(ring_row)] at offset p % page_size; p < 0
-    gives slot -1."""
-    import numpy as np
-    ring_row = np.asarray(ring_row, dtype=np.int64)
-    p = np.asarray(positions, dtype=np.int64)
-    pc = np.maximum(p, 0)
-    slots = ring_row[(pc // page_size) % len(ring_row)] * page_size + pc % page_size
-    return np.where(p < 0, -1, slots).astype(np.int32)
+def tl_slot_mapping(tables, positions, page_size: int, num_pages: int, ring_pages: int = 0, out=None,
+                    stream=None):
+    """SLOT_MAPPING (ring_pages = 0) or WINDOW_SLOT_MAPPING (ring_pages = R): slots int32
+    [B, T] of positions [B, T] through tables [B, width] (device int32 tensors)."""
+    import torch
+    if positions.dim() == 1:
+        positions = positions.reshape(1, -1)
+    if tables.dim() == 1:
+        tables = tables.reshape(1, -1)
+    B, T = positions.shape
+    if out is None:
+        out = torch.empty((B, T), dtype=torch.int32, device=positions.device)
+    _check(lib().tl_slot_mapping(tables.data_ptr(), int(tables.shape[1]), ring_pages, positions.data_ptr(), B, T,
+                                 page_size, num_pages, out.data_ptr(), _stream(stream)))
+    return out
 
 
 def tl_gated_delta_rule_decode(state_pool, q, k, v, g, beta, state_slots, positions, out=None, stream=None):
@@ -374,5 +380,5 @@ def tl_abi_version() -> int:
 
 
 __all__ = ["KVPool", "TLError", "tl_kv_cache_write", "tl_paged_attn_decode", "tl_paged_attn_prefill",
-           "tl_kv_gather", "tl_paged_attn_decode_workspace_size", "tl_paged_attn_prefill_workspace_size",
+           "tl_kv_gather", "tl_slot_mapping", "tl_paged_attn_decode_workspace_size", "tl_paged_attn_prefill_workspace_size",
            "tl_last_error", "tl_abi_version", "lib"]

@@ -458,6 +458,57 @@ int tl_kv_copy_pages(const tl_kv_pool* pool, const int32_t* src_pages, const int
   return ok();
 }
 
+int tl_slot_mapping(const int32_t* tables, int32_t width, int32_t ring_pages, const int32_t* positions,
+                    int32_t batch, int32_t tokens_per_row, int32_t page_size, int32_t num_pages, int32_t* slots,
+                    void* stream) {
+  const char* fn = "tl_slot_mapping";
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if (tokens_per_row < 0) return fail(TL_ERR_INVALID, "%s: tokens_per_row (%d) must be >= 0", fn, tokens_per_row);
+  if (width <= 0) return fail(TL_ERR_INVALID, "%s: width (%d) must be > 0", fn, width);
+  if (ring_pages < 0 || ring_pages > width)
+    return fail(TL_ERR_INVALID, "%s: ring_pages (%d) must be in [0, width = %d]", fn, ring_pages, width);
+  if (!is_pow2(page_size) || page_size < 8 || page_size > 1024)
+    return fail(TL_ERR_UNSUPPORTED, "%s: page_size (%d) must be a power of two in [8, 1024]", fn, page_size);
+  if (num_pages <= 0) return fail(TL_ERR_INVALID, "%s: num_pages (%d) must be > 0", fn, num_pages);
+  if ((int64_t)num_pages * page_size >= ((int64_t)1 << 31))
+    return fail(TL_ERR_UNSUPPORTED, "%s: num_pages * page_size must be < 2^31", fn);
+  if ((int64_t)batch * tokens_per_row >= ((int64_t)1 << 31))
+    return fail(TL_ERR_UNSUPPORTED, "%s: batch * tokens_per_row must be < 2^31", fn);
+  if (batch == 0 || tokens_per_row == 0) return ok();
+  if (!tables) return fail(TL_ERR_INVALID, "%s: tables is NULL", fn);
+  if (!positions) return fail(TL_ERR_INVALID, "%s: positions is NULL", fn);
+  if (!slots) return fail(TL_ERR_INVALID, "%s: slots is NULL", fn);
+  if (!aligned(tables, 4) || !aligned(positions, 4) || !aligned(slots, 4))
+    return fail(TL_ERR_INVALID, "%s: tables/positions/slots are not 4-byte aligned", fn);
+  hipStream_t s = (hipStream_t)stream;
+  int rc;
+  if (validate_mode()) {
+    std::vector<int32_t> pos, tab;
+    if ((rc = copy_to_host(fn, "positions", positions, (size_t)batch * tokens_per_row, pos, s))) return rc;
+    if ((rc = copy_to_host(fn, "tables", tables, (size_t)batch * width, tab, s))) return rc;
+    for (int32_t b = 0; b < batch; ++b)
+      for (int32_t t = 0; t < tokens_per_row; ++t) {
+        const int32_t p = pos[(size_t)b * tokens_per_row + t];
+        if (p < 0) continue;
+        int64_t blk = p / page_size;
+        if (ring_pages > 0) blk %= ring_pages;
+        if (blk >= width)
+          return fail(TL_ERR_INVALID, "%s: positions[%d][%d] = %d is past the table (TL_VALIDATE)", fn, b, t, p);
+        const int32_t page = tab[(size_t)b * width + blk];
+        if (page < 0 || page >= num_pages)
+          return fail(TL_ERR_INVALID, "%s: tables[%d][%lld] = %d is not a page of the pool (TL_VALIDATE)", fn, b,
+                      (long long)blk, page);
+      }
+  }
+  tl::SlotMapArgs a;
+  a.tables = tables; a.positions = positions; a.slots = slots;
+  a.batch = batch; a.tokens = tokens_per_row; a.width = width; a.ring = ring_pages;
+  a.page_shift = log2i(page_size); a.num_pages = num_pages;
+  hipError_t e = tl::launch_slot_mapping(a, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
 int tl_kv_gather(const tl_kv_pool* pool, const int32_t* block_table_row, int32_t length, void* k_out, void* v_out,
                  float* k_scale_out, float* v_scale_out, void* stream) {
   const char* fn = "tl_kv_gather";

@@ -121,6 +121,14 @@ struct GatherArgs {
   float* v_scale_out;
 };
 
+// SLOT_MAPPING (block tables) and WINDOW_SLOT_MAPPING (rings)
+struct SlotMapArgs {
+  const int32_t* tables;     // [batch][width]
+  const int32_t* positions;  // [batch][tokens]
+  int32_t* slots;            // [batch][tokens]
+  int batch, tokens, width, ring, page_shift, num_pages;
+};
+
 struct DecodeArgs {
   PoolArgs pool;
   const float* q;
@@ -170,6 +178,7 @@ struct GdnArgs {
 // Each returns hipSuccess or the launch error.  Arguments are already validated.
 hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int kv_dtype, hipStream_t s);
+hipError_t launch_slot_mapping(const SlotMapArgs& a, hipStream_t s);
 int decode_split_keys(int kv_dtype, int group, int page_size);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s);
 int prefill_tokens_per_wg(int group);

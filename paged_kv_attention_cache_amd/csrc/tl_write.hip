@@ -1,7 +1,8 @@
 // KV_CACHE_WRITE: scatter new K/V rows into the page pool at their slots
 // ("How serving works in Tlaloc", section 2, KV_CACHE_WRITE bullet; slot -1 is a pad
-// whose KV is never written, section 1).  Also the test gather that copies a
-// sequence's stored rows out in logical order.
+// whose KV is never written, section 1), the slot mapping that names those slots
+// (section 3: SLOT_MAPPING, and WINDOW_SLOT_MAPPING for a ring), and the test gather
+// that copies a sequence's stored rows out in logical order.
 //
 // Mapping: 8 lanes own one (token, kv head) row of D values; the 8 rows of a wave
 // are 8 consecutive tokens of one head, and each lane holds whole 16-byte store
@@ -212,6 +213,27 @@ __global__ __launch_bounds__(WG) void gather_kernel(GatherArgs a) {
   }
 }
 
+// Slot of each (row, token): the block's table entry times the page size plus the
+// offset in the page; on a ring, block j is on entry j % R.  A pad (position < 0), a
+// block past the table and an entry outside the pool all give -1, which the write
+// skips.  One thread per token.
+__global__ __launch_bounds__(WG) void slot_mapping_kernel(SlotMapArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+  if (i >= (int64_t)a.batch * a.tokens) return;
+  const int64_t b = i / a.tokens;
+  const int p = a.positions[i];
+  int32_t slot = -1;
+  if (p >= 0) {
+    int blk = p >> a.page_shift;
+    if (a.ring > 0) blk %= a.ring;
+    if (blk < a.width) {
+      const int page = a.tables[b * a.width + blk];
+      if (page >= 0 && page < a.num_pages) slot = (page << a.page_shift) | (p & ((1 << a.page_shift) - 1));
+    }
+  }
+  a.slots[i] = slot;
+}
+
 template <int KVT>
 hipError_t write_dispatch(const WriteArgs& a, hipStream_t s) {
   // rows are counted in whole blocks of 8 tokens (the tail block's missing tokens return)
@@ -242,6 +264,13 @@ hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s) {
     case KV_FP8U: return write_dispatch<KV_FP8U>(a, s);
     default: return write_dispatch<KV_INT8>(a, s);
   }
+}
+
+hipError_t launch_slot_mapping(const SlotMapArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.batch * a.tokens;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((unsigned)((n + WG - 1) / WG)), dim3(WG), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather(const GatherArgs& a, int kv_dtype, hipStream_t s) {

@@ -18,6 +18,18 @@ from tests.test_gpu_parity import TOL, assert_pool_equal, torch_cuda  # noqa: F4
 pytestmark = pytest.mark.gpu
 
 
+def ring_slots_gpu(ring_row, p, S, num_pages):
+    """WINDOW_SLOT_MAPPING through the library (tl_slot_mapping on the device), checked
+    against the oracle's ring_slots for the same positions."""
+    import torch
+    import paged_kv_attention_cache_amd as tl
+    ring_row = np.asarray(ring_row, dtype=np.int32)
+    got = tl.tl_slot_mapping(torch.from_numpy(ring_row).cuda(), torch.from_numpy(np.asarray(p, np.int32)).cuda(), S,
+                             num_pages, ring_pages=len(ring_row)).cpu().numpy().reshape(-1)
+    assert np.array_equal(got, oracle.ring_slots(ring_row, p, S)), "ring slot mapping differs from the oracle"
+    return got
+
+
 def kv_rows(rng, n, Hkv, D):
     k = (rng.standard_normal((n, Hkv, D)) * rng.uniform(0.5, 2.0, (n, Hkv, 1))).astype(np.float32)
     v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
@@ -48,7 +60,7 @@ class RingCase:
                 if p.size == 0:
                     continue
                 ks.append(self.kv[b][0][p]); vs.append(self.kv[b][1][p])
-                ss_gpu.append(tl.ring_slot_mapping(self.ring[b], p, self.S))
+                ss_gpu.append(ring_slots_gpu(self.ring[b], p, self.S, self.P))
                 ss_orc.append(oracle.ring_slots(self.ring[b], p, self.S))
             k, v = np.concatenate(ks), np.concatenate(vs)
             tl.tl_kv_cache_write(gpu_pool, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
@@ -179,7 +191,7 @@ def test_chunked_ring_prefill_parity_and_equals_full_table(torch_cuda, dt, Hq, H
             if p.size == 0:
                 continue
             ks.append(c.kv[b][0][p]); vs.append(c.kv[b][1][p])
-            rs.append(tl.ring_slot_mapping(c.ring[b], p, S))
+            rs.append(ring_slots_gpu(c.ring[b], p, S, c.P))
             os_.append(oracle.ring_slots(c.ring[b], p, S))
             fs.append((tables[b, p // S] * S + p % S).astype(np.int32))
         k, v = np.concatenate(ks), np.concatenate(vs)
@@ -220,7 +232,7 @@ def test_prefill_chunk_too_long_for_the_ring_follows_the_age_mask(torch_cuda):
         p = np.arange(p0, min(total, p0 + chunk))
         k, v = c.kv[0][0][p], c.kv[0][1][p]
         kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
-        tl.tl_kv_cache_write(gp, kt, vt, torch.from_numpy(tl.ring_slot_mapping(c.ring[0], p, S)).cuda())
+        tl.tl_kv_cache_write(gp, kt, vt, torch.from_numpy(ring_slots_gpu(c.ring[0], p, S, c.P)).cuda())
         tl.tl_kv_cache_write(fp, kt, vt, torch.from_numpy((tables[0, p // S] * S + p % S).astype(np.int32)).cuda())
         op.write(k, v, oracle.ring_slots(c.ring[0], p, S))
         pos = p[None].astype(np.int32)
