@@ -4,8 +4,9 @@ Writes and gathered KV: byte for byte, whole pools including untouched sentinel
 pages and scale arrays.  Attention outputs: worst per-row error
 max_d|o - o_ref| / max_d|o_ref| <= 2e-5 (f32 and bf16 KV) or 1e-2 (fp8 KV against
 the dequantised oracle); rows with no visible key must be exactly 0.
-Full-size configurations are checked on sampled sequences/tokens, which the
-oracle recomputes from a contiguous copy of the sequence's stored history.
+Full-size configurations are checked on every decode sequence and on every live
+prefill token (long rows: both edges of every query tile plus a random sample),
+against the oracle over a contiguous copy of the sequence's stored history.
 """
 import numpy as np
 import pytest
@@ -340,72 +341,96 @@ def test_prefill_batch_invariance_and_decode_agreement(torch_cuda):
 
 
 # ============================================================ full-size configs
-def _stored_values(wl, b):
-    k, v = wl.seq_kv(b)
-    kr, ks = E.encode_kv(k, wl.kv_dtype)
-    vr, vs = E.encode_kv(v, wl.kv_dtype)
-    return (kr, ks, vr, vs), E.kv_values(kr, ks, wl.kv_dtype), E.kv_values(vr, vs, wl.kv_dtype)
+# Scaled fp8 widens codes exactly on the GPU (one f32 rounding for each scale product),
+# so besides the stated 1e-2 it is held to this internal bound: a regression to 1e-3
+# would fail it.
+TIGHT = {"fp8": 1e-4}
 
 
-def _check_seq_written(tl, torch, wl, gp, tables, b):
-    L = wl.context_len(b)
-    (kr, ks, vr, vs), _, _ = _stored_values(wl, b)
-    gk, gv, gks, gvs = tl.tl_kv_gather(gp, tables[b], L)
+def _gathered_digest(tl, torch, gp, table_row, L):
+    from tests.fullsize import digest
+    gk, gv, gks, gvs = tl.tl_kv_gather(gp, table_row, L)
     torch.cuda.synchronize()
-    assert np.array_equal(gk.cpu().view(torch.uint8).numpy().reshape(-1), kr.view(np.uint8).reshape(-1))
-    assert np.array_equal(gv.cpu().view(torch.uint8).numpy().reshape(-1), vr.view(np.uint8).reshape(-1))
-    if ks is not None:
-        assert np.array_equal(gks.cpu().numpy(), ks) and np.array_equal(gvs.cpu().numpy(), vs)
+    cpu = [None if t is None else t.cpu().contiguous().view(torch.uint8).numpy() for t in (gk, gv, gks, gvs)]
+    return digest(*cpu)
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c5", "c2r"])
-def test_full_decode_config_sampled(torch_cuda, cfg):
-    """c2r is c2's layer with window 2,048 on rings of 129 pages: its reference is the
-    windowed attention over the sequence's whole contiguous history."""
+@pytest.mark.parametrize("cfg", ["c2", "c5", "c2r", "c5u", "c2i"])
+def test_full_decode_config_every_row(torch_cuda, cfg):
+    """Every sequence of the full-size decode workload, in the launch configuration the
+    bench times, against the oracle over the sequence's contiguous stored history; and
+    (full tables) every sequence's stored rows byte for byte, through a digest.  c2r is
+    c2's layer with window 2,048 on rings of 129 pages: its reference is the windowed
+    attention over the whole history."""
     torch = torch_cuda
     import paged_kv_attention_cache_amd as tl
+    from tests import fullsize as F
     wl = W.make(cfg)
-    gp = R.make_pool(wl)
-    R.write_history(gp, wl)
-    st = R.DecodeStep(wl, gp)
-    out = st.run().cpu().numpy()
-    L = wl.seq_lens
-    picks = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, wl.batch - 1, wl.batch // 2})
-    q = wl.decode_q()
-    for b in picks:
-        if wl.ring_pages == 0:
-            _check_seq_written(tl, torch, wl, gp, st.tables, b)
-        _, Kv, Vv = _stored_values(wl, b)
-        ref = oracle.paged.attend_history(q[b:b + 1], Kv, Vv, np.array([L[b] - 1]), wl.window, wl.scale)
-        err = row_rel_err(out[b:b + 1], ref)
-        assert err <= TOL[wl.kv_dtype], f"{cfg} seq {b} (L={L[b]}): {err:.3e}"
-    assert np.all(np.isfinite(out))
+    order = [int(b) for b in np.argsort(-wl.seq_lens, kind="stable")]  # longest first
+    tol, tight = TOL[wl.kv_dtype], TIGHT.get(wl.kv_dtype, TOL[wl.kv_dtype])
+    with F.pool() as ex:
+        futs = [ex.submit(F.decode_row, cfg, b) for b in order]
+        gp = R.make_pool(wl)
+        R.write_history(gp, wl)
+        st = R.DecodeStep(wl, gp)
+        out = st.run().cpu().numpy()
+        assert np.all(np.isfinite(out))
+        worst = 0.0
+        for f in futs:
+            b, dg, ref = f.result()
+            if wl.ring_pages == 0:
+                assert _gathered_digest(tl, torch, gp, st.tables[b], int(wl.seq_lens[b])) == dg, \
+                    f"{cfg} seq {b}: stored K/V differ from the oracle's encoding"
+            err = row_rel_err(out[b], ref)
+            assert err <= tol and err <= tight, f"{cfg} seq {b} (L={wl.seq_lens[b]}): {err:.3e}"
+            worst = max(worst, err)
+    print(f"{cfg}: all {wl.batch} sequences checked, worst row error {worst:.3e}")
+
+
+def _prefill_tokens(wl, b, rng):
+    """Tokens of row b to check: every live token when the row's history is short (c3);
+    at long context, both edges of every wave's query tile (32/G tokens) plus a random
+    sample of 64."""
+    pos = wl.row_positions()[b]
+    live = np.nonzero(pos >= 0)[0]
+    if wl.context_len(b) <= 4096:
+        return live
+    tpw = 32 // wl.group
+    edges = live[(live % tpw == 0) | (live % tpw == tpw - 1)]
+    return np.unique(np.concatenate([edges, rng.choice(live, size=min(64, len(live)), replace=False)]))
 
 
 @pytest.mark.parametrize("cfg", ["c3", "c4", "c4w"])
-def test_full_prefill_config_sampled(torch_cuda, cfg):
+def test_full_prefill_config_every_tile(torch_cuda, cfg):
     torch = torch_cuda
     import paged_kv_attention_cache_amd as tl
+    from tests import fullsize as F
     wl = W.make(cfg)
-    gp = R.make_pool(wl)
-    R.write_history(gp, wl)
-    st = R.PrefillStep(wl, gp)
-    out = st.run().cpu().numpy()
-    pos = wl.row_positions()
-    T = wl.tokens_per_row
     rng = np.random.default_rng(77)
+    tasks = []
     for b in range(wl.batch):
-        _check_seq_written(tl, torch, wl, gp, st.tables, b)
-        live = np.nonzero(pos[b] >= 0)[0]
-        pads = np.nonzero(pos[b] < 0)[0]
-        assert np.all(out[b, pads] == 0)
-        ts = np.unique(np.concatenate([live[:3], live[-3:], rng.choice(live, size=min(10, len(live)), replace=False)]))
-        _, Kv, Vv = _stored_values(wl, b)
-        q = wl.prefill_rows(b)[0]
-        ref = oracle.paged.attend_history(q[ts], Kv, Vv, pos[b, ts], wl.window, wl.scale)
-        err = row_rel_err(out[b, ts], ref)
-        assert err <= TOL[wl.kv_dtype], f"{cfg} row {b}: {err:.3e}"
-    assert np.all(np.isfinite(out))
+        ts = _prefill_tokens(wl, b, rng)
+        for a in range(0, len(ts), 64):
+            tasks.append((b, ts[a:a + 64]))
+    tol = TOL[wl.kv_dtype]
+    with F.pool() as ex:
+        futs = [ex.submit(F.prefill_rows, cfg, b, ts) for b, ts in tasks]
+        gp = R.make_pool(wl)
+        R.write_history(gp, wl)
+        st = R.PrefillStep(wl, gp)
+        out = st.run().cpu().numpy()
+        assert np.all(np.isfinite(out))
+        pos = wl.row_positions()
+        assert np.all(out[pos < 0] == 0), "pad rows must be exactly 0"
+        digests = {b: _gathered_digest(tl, torch, gp, st.tables[b], wl.context_len(b)) for b in range(wl.batch)}
+        worst, n = 0.0, 0
+        for f in futs:
+            b, ts, dg, ref = f.result()
+            assert digests[b] == dg, f"{cfg} row {b}: stored K/V differ from the oracle's encoding"
+            err = row_rel_err(out[b, ts], ref)
+            assert err <= tol, f"{cfg} row {b}: {err:.3e}"
+            worst, n = max(worst, err), n + len(ts)
+    print(f"{cfg}: {n} tokens checked, worst row error {worst:.3e}")
 
 
 def test_fp8u_write_saturates_and_rounds_like_the_oracle(torch_cuda):
