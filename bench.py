@@ -60,6 +60,71 @@ def traffic_record(cfg: str):
     return rec.get("bytes_per_launch")
 
 
+FLUSH_BYTES = 512 << 20  # larger than the 256 MB last-level cache (MALL) plus the L2s
+
+
+def timed_steps(write, attend, steps: int):
+    """The contract loop: exactly `steps` back-to-back steps (the step's write, then its
+    attention call) between synchronisations, wall clock; the attention calls are also
+    bracketed by HIP events on their stream.  Returns (ms per step, mean attention ms)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if write is not None:
+            write()
+        ev[i][0].record(stream)
+        attend()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+_flush = None
+
+
+def _flush_caches():
+    """Read FLUSH_BYTES of scratch with plain (cache-allocating) loads: every line an
+    earlier call left in the L2s or the MALL is evicted, and dirty ones are written
+    back now, not during the next timed call (a flush that wrote its scratch would
+    leave its own dirty lines to be written back inside the timed call)."""
+    import ctypes
+    import torch
+    global _flush
+    if _flush is None:
+        from paged_kv_attention_cache_amd import _build
+        L = ctypes.CDLL(_build.STREAM_LIB)
+        L.tl_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+        _flush = (L, torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda"),
+                  torch.zeros(1, dtype=torch.int32, device="cuda"))
+    L, buf, sink = _flush
+    rc = L.tl_stream_read(buf.data_ptr(), FLUSH_BYTES, sink.data_ptr(), 0, 2048, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"tl_stream_read: HIP error {rc}")
+
+
+def flushed_calls(attend, calls: int):
+    """Each attention call timed alone with HIP events on its stream, after FLUSH_BYTES of
+    scratch have been read (untimed), so that no input is served from a cache the
+    previous call filled.  Returns median, min and mean milliseconds."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i in range(calls):
+        _flush_caches()
+        ev[i][0].record(stream)
+        attend()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": float(np.median(ms)), "min_ms": float(ms.min()), "mean_ms": float(ms.mean()),
+            "calls": calls}
+
+
 def run_config(name: str, steps: int, warmup: int):
     import torch
     from paged_kv_attention_cache_amd import accounting as A
@@ -74,22 +139,12 @@ def run_config(name: str, steps: int, warmup: int):
     torch.cuda.synchronize()
     log(f"[bench] {name}: pool {pool.nbytes() / 2**30:.2f} GiB, {hist} history tokens written "
         f"({time.time() - t0:.1f} s setup)")
-    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(steps):
-        step.write()
-        ev[i][0].record(stream)
-        step.attend()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    ms_step = wall * 1e3 / steps
+    ms_step, attn_back_to_back = timed_steps(step.write, step.attend, steps)
+    attn = flushed_calls(step.attend, steps)
+    attn_ms = attn["median_ms"]
 
     hist_write = history_write_rate(wl, pool) if wl.kind == "decode" else None
 
@@ -99,13 +154,16 @@ def run_config(name: str, steps: int, warmup: int):
         wr_bytes = A.write_bytes(step.slots.cpu().numpy(), wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
         res = {
             "workload": wl.name, "kind": "decode", "batch": wl.batch, "kv_dtype": wl.kv_dtype,
-            "ms_per_step": ms_step, "attn_ms": attn_ms,
+            "ms_per_step": ms_step, "attn_ms": attn_ms, "attn_ms_min": attn["min_ms"],
+            "attn_ms_back_to_back": attn_back_to_back,
             "step_GBps": (attn_bytes + wr_bytes) / (ms_step * 1e-3) / 1e9,
             "attn_GBps": attn_bytes / (attn_ms * 1e-3) / 1e9,
             "attn_bytes": attn_bytes, "write_bytes": wr_bytes,
             "flops": A.decode_flops(wl.seq_lens, wl.num_q_heads, wl.head_dim, wl.window),
         }
         res["hbm_frac"] = res["attn_GBps"] / HBM_PEAK_GBPS
+        res["hbm_frac_min"] = attn_bytes / (attn["min_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
+        res["hbm_frac_back_to_back"] = attn_bytes / (attn_back_to_back * 1e-3) / 1e9 / HBM_PEAK_GBPS
         res.update(hist_write)
     else:
         pos = wl.row_positions()
@@ -114,11 +172,13 @@ def run_config(name: str, steps: int, warmup: int):
         res = {
             "workload": wl.name, "kind": "prefill", "batch": wl.batch, "tokens_per_row": wl.tokens_per_row,
             "window": wl.window, "kv_dtype": wl.kv_dtype, "ms_per_step": ms_step, "attn_ms": attn_ms,
+            "attn_ms_min": attn["min_ms"], "attn_ms_back_to_back": attn_back_to_back,
             "flops": flops, "write_bytes": wr_bytes,
             "attn_TFLOPs": flops / (attn_ms * 1e-3) / 1e12,
             "step_TFLOPs": flops / (ms_step * 1e-3) / 1e12,
         }
         res["mfma_frac"] = res["attn_TFLOPs"] / MFMA_F32_PEAK_TFLOPS
+        res["mfma_frac_back_to_back"] = flops / (attn_back_to_back * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS
     del step, pool
     torch.cuda.empty_cache()
     return wl, res
@@ -136,27 +196,25 @@ def run_gdn(name: str, steps: int, warmup: int):
     ins = [torch.from_numpy(x).cuda() for x in wl.step_inputs(0)]
     st, pt = torch.from_numpy(slots).cuda(), torch.from_numpy(pos).cuda()
     out = torch.empty_like(ins[2])
+    def call():
+        tl_gated_delta_rule_decode(pool, *ins, st, pt, out=out)
+
     for _ in range(warmup):
-        tl_gated_delta_rule_decode(pool, *ins, st, pt, out=out)
+        call()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        tl_gated_delta_rule_decode(pool, *ins, st, pt, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
+    ms_step, back_to_back = timed_steps(None, call, steps)
+    attn = flushed_calls(call, steps)  # the 168 MB state pool would otherwise stay in the MALL
+    ms = attn["median_ms"]
     live = int(np.count_nonzero(slots >= 0))
     fresh = int(np.count_nonzero((slots >= 0) & (pos == 0)))
     D, H = wl.head_dim, wl.num_heads
     # state read (not for fresh rows) and written, q k v read and o written, g and beta, slots, positions
     nbytes = (live * 2 - fresh) * H * D * D * 4 + wl.batch * H * (4 * D * 4 + 8) + wl.batch * 8
-    return wl, {"kind": "gdn", "workload": wl.name, "attn_ms": ms, "attn_bytes": nbytes,
+    return wl, {"kind": "gdn", "workload": wl.name, "attn_ms": ms, "attn_ms_min": attn["min_ms"],
+                "attn_ms_back_to_back": back_to_back, "attn_bytes": nbytes,
                 "attn_GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                "ms_per_step": wall * 1e3 / steps}
+                "hbm_frac_back_to_back": nbytes / (back_to_back * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "ms_per_step": ms_step}
 
 
 def history_write_rate(wl, pool, reps: int = 10):
@@ -168,56 +226,88 @@ def history_write_rate(wl, pool, reps: int = 10):
     from paged_kv_attention_cache_amd import tl_kv_cache_write
     k, v, slots = next(wl.history_batches())
     dk, dv, ds = R._t(k, "cuda"), R._t(v, "cuda"), R._t(slots, "cuda")
+
+    def call():
+        tl_kv_cache_write(pool, dk, dv, ds)
+
     for _ in range(2):
-        tl_kv_cache_write(pool, dk, dv, ds)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        call()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        tl_kv_cache_write(pool, dk, dv, ds)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    t = flushed_calls(call, reps)
+    ms = t["median_ms"]
     nbytes = A.write_bytes(slots, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
     return {"hist_write_tokens": int(len(slots)), "hist_write_bytes": nbytes, "hist_write_ms": ms,
-            "hist_write_GBps": nbytes / (ms * 1e-3) / 1e9}
+            "hist_write_ms_min": t["min_ms"], "hist_write_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hist_write_hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
-def cpu_baseline(target_s: float = 12.0, cap_s: float = 30.0):
-    """The oracle on a time-bounded sample of the headline decode workload, on this host.
+_CPU_WL = None
 
-    Sequences of the workload are processed in order, each one's pool write then its
-    decode attention, until about target_s seconds of CPU work (passes over the whole
-    batch repeat if one pass is shorter); the rate uses the same algorithmic bytes as
-    the GPU figure."""
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
+    global _CPU_LIMIT
+    _CPU_LIMIT = threadpool_limits(1)  # one BLAS thread per worker process
 
+
+def _cpu_sequence_step(b: int):
+    """One sequence-step of the headline decode workload on the oracle: the sequence's
+    pool write, then its decode attention.  The sequence's own pages form the pool (in
+    the workload's shuffled order); its inputs are drawn before the clock starts."""
     import oracle
     from paged_kv_attention_cache_amd import accounting as A
     from paged_kv_attention_cache_amd import workloads as W
+    global _CPU_WL
+    if _CPU_WL is None:
+        _CPU_WL = W.make("c2")
+    wl = _CPU_WL
+    L, S = int(wl.seq_lens[b]), wl.page_size
+    n = -(-L // S)
+    local = np.argsort(np.argsort(wl.block_tables[b, :n])).astype(np.int32)  # page ranks: the same shuffle
+    table = np.full((1, wl.max_blocks), -1, np.int32)
+    table[0, :n] = local
+    slots = (local[np.arange(L) // S] * S + np.arange(L) % S).astype(np.int32)
+    k, v = wl.seq_kv(b)
+    q = wl.decode_q(b)[None]
+    pool = oracle.KVPool(n, S, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    t0 = time.perf_counter()
+    pool.write(k, v, slots)
+    oracle.decode(pool, q, table, wl.seq_lens[b:b + 1], 0, wl.scale)
+    dt = time.perf_counter() - t0
+    nbytes = A.decode_bytes(wl.seq_lens[b:b + 1], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, S, wl.kv_dtype)
+    return os.getpid(), dt, nbytes, L
 
-    wl = W.make("c2")
-    q = wl.decode_q()
-    done, positions, nbytes, dt = 0, 0, 0, 0.0
-    pool = oracle.KVPool(wl.num_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)  # resident, untimed
-    with threadpool_limits(1):
-        while dt < target_s and dt < cap_s:
-            b = done % wl.batch
-            k, v = wl.seq_kv(b)  # inputs are drawn outside the timed part
-            t0 = time.perf_counter()
-            pool.write(k, v, wl.slots_for(b, np.arange(int(wl.seq_lens[b]))))
-            oracle.decode(pool, q, wl.block_tables, wl.seq_lens, 0, wl.scale, seqs=[b])
-            dt += time.perf_counter() - t0
-            done += 1
-            positions += int(wl.seq_lens[b])
-            nbytes += A.decode_bytes(wl.seq_lens[b:b + 1], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                     wl.page_size, wl.kv_dtype)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence-steps of the headline decode workload (sequences in order, "
-                      f"{positions} positions): each one's pool write then its decode attention, numpy f64, "
-                      f"one thread; {dt:.1f} s",
-            "seconds": dt}
+
+def cpu_baseline(target_s: float = 12.0, cap_s: float = 60.0):
+    """The oracle on a time-bounded sample of the headline decode workload, on this host's
+    cores: one worker process per core this process may use (at most 16, the host share
+    of one GPU), each with one BLAS thread, taking sequence-steps in order (passes over
+    the batch repeat) until the busiest worker has spent about target_s seconds.  The rate
+    is the sample's algorithmic bytes (as for the GPU figure) over that busiest worker's
+    compute time, i.e. the time of a run in which all workers start together."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    batch = 64
+    busy, nbytes, done, positions = {}, 0, 0, 0
+    t_start = time.perf_counter()
+    with ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn"), initializer=_cpu_worker_init) as ex:
+        while (not busy or max(busy.values()) < target_s) and time.perf_counter() - t_start < cap_s:
+            futs = [ex.submit(_cpu_sequence_step, (done + i) % batch) for i in range(2 * cores)]
+            for f in futs:
+                pid, dt, nb, L = f.result()
+                busy[pid] = busy.get(pid, 0.0) + dt
+                nbytes += nb
+                positions += L
+            done += len(futs)
+    t = max(busy.values())
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": len(busy), "kind": "oracle",
+            "sample": f"{done} sequence-steps of the headline decode workload (sequences in order, passes "
+                      f"repeating; {positions} positions): each one's pool write then its decode attention, "
+                      f"numpy f64, on {len(busy)} worker processes of one BLAS thread each; busiest worker "
+                      f"{t:.1f} s of compute (inputs drawn outside the clock)",
+            "seconds": t}
 
 
 # ------------------------------------------------------------------ rocprofv3 summaries
@@ -251,6 +341,39 @@ def _counter_means(d: str, counter: str):
             continue
         acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def hbm_ceiling(gib: int = 4, reps: int = 20):
+    """Streaming-read ceiling of this GPU's HBM: a 4 GiB buffer read once per call with
+    plain and with nontemporal 16-byte loads (libtl_stream.so), at several grid sizes,
+    each call after FLUSH_BYTES of scratch traffic, timed with HIP events; median GB/s.
+    Context for the roofline fractions, whose denominator stays the published 8 TB/s."""
+    import ctypes
+    import torch
+    from paged_kv_attention_cache_amd import _build
+    L = ctypes.CDLL(_build.STREAM_LIB)
+    L.tl_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for nt in (0, 1):
+        for wg in (1024, 2048, 4096, 8192):
+            def call():
+                rc = L.tl_stream_read(buf.data_ptr(), n, sink.data_ptr(), nt, wg, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"tl_stream_read: HIP error {rc}")
+            call()
+            t = flushed_calls(call, reps)
+            key = f"{'nontemporal' if nt else 'plain'}_wg{wg}"
+            res[key] = {"median_GBps": n / (t["median_ms"] * 1e-3) / 1e9, "max_GBps": n / (t["min_ms"] * 1e-3) / 1e9,
+                        "median_ms": t["median_ms"]}
+            log(f"[bench] stream read {key}: {res[key]['median_GBps']:.0f} GB/s median")
+    best = max(res.items(), key=lambda kv: kv[1]["median_GBps"])
+    print(json.dumps({"hbm_stream_read": res, "best": best[0], "best_median_GBps": best[1]["median_GBps"],
+                      "bytes_per_call": n, "calls": reps, "peak_GBps": HBM_PEAK_GBPS}), flush=True)
 
 
 def copy_calibration(gib: int = 1, reps: int = 3):
@@ -350,6 +473,9 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
         copy_calibration()
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--hbm-ceiling":
+        hbm_ceiling()
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -396,6 +522,13 @@ def main():
                 "unit": "TFLOP/s", "frac": head["attn_TFLOPs"] / MFMA_F32_PEAK_TFLOPS,
                 "kernel": "prefill kernel (one tl_paged_attn_prefill call)", "per_launch_flops": head["flops"]}
     roof["traffic"] = traffic_record(names[0])
+    roof["timing"] = (f"median of {args.steps} calls, each after {FLUSH_BYTES >> 20} MiB of cache-evicting "
+                      f"traffic, HIP events on the launch stream")
+    roof["avg_launch_ms"] = head["attn_ms"]
+    if "hbm_frac_back_to_back" in head:
+        roof["frac_back_to_back"] = head["hbm_frac_back_to_back"]
+    elif "mfma_frac_back_to_back" in head:
+        roof["frac_back_to_back"] = head["mfma_frac_back_to_back"]
 
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

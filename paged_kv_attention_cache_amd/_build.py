@@ -12,6 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtl.so")
 SOURCES = ["tl_api.hip", "tl_write.hip", "tl_decode.hip", "tl_prefill.hip", "tl_gdn.hip", "tl_alloc.hip"]
+STREAM_SOURCE = "tl_stream.hip"  # measurement support: built as libtl_stream.so
+STREAM_LIB = os.path.join(HERE, "libtl_stream.so")
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
 HIP_FLAGS = [
@@ -52,10 +54,13 @@ def build(verbose: bool = False, extra_flags=(), out: str | None = None, build_d
         return obj
 
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(one, SOURCES))
+        objs = list(ex.map(one, SOURCES + [STREAM_SOURCE]))
     tmp = lib + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs[:-1]])
     os.replace(tmp, lib)
+    if out is None:  # the HBM streaming-read measurement library (bench.py --hbm-ceiling)
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", STREAM_LIB + ".tmp", objs[-1]])
+        os.replace(STREAM_LIB + ".tmp", STREAM_LIB)
     return lib
 
 

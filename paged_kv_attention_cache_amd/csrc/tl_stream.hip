@@ -1,0 +1,57 @@
+// Streaming-read ceiling of HBM on this GPU: every 16-byte unit of a buffer is read
+// once, with plain or nontemporal loads (the decode kernels read the KV pages with
+// nontemporal loads).  This is measurement support for the roofline figures, built as
+// its own small library (libtl_stream.so) beside libtl.so; the attention path never
+// calls it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u4 ld(const u4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
+}
+
+// Each thread reads four units per trip, a grid stride apart, and folds them into one
+// word; the word is stored only if it equals a value the data never produces here, so
+// the loads stay live without any real store traffic.
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u4* p, int64_t units, unsigned* sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 3 * stride < units; i += 4 * stride) {
+    const u4 a = ld<NT>(p + i), b = ld<NT>(p + i + stride), c = ld<NT>(p + i + 2 * stride),
+             d = ld<NT>(p + i + 3 * stride);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  for (; i < units; i += stride) {
+    const u4 a = ld<NT>(p + i);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Read `bytes` (a multiple of 16, 16-byte aligned) of device memory at `src` once.
+// sink: one device word, written only in the unlikely case above.  Returns 0, or the
+// HIP error code of the launch.
+int tl_stream_read(const void* src, size_t bytes, unsigned* sink, int nontemporal, int workgroups, void* stream) {
+  const int64_t units = (int64_t)(bytes / 16);
+  if (units <= 0 || workgroups <= 0) return 0;
+  const u4* p = static_cast<const u4*>(src);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3((unsigned)workgroups), dim3(256), 0, s, p, units, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)workgroups), dim3(256), 0, s, p, units, sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
