@@ -8,11 +8,12 @@ other configurations (batched and long-context prefill in f32 TFLOP/s, fp8 KV
 decode in GB/s) are measured in the same run and reported under "secondary".
 
 Inputs are resident in HBM before the timed region.  Each configuration:
-W untimed warm-up steps, then exactly K timed steps bracketed by
-torch.cuda.synchronize(); the attention call is also bracketed by HIP events on
-the stream it runs on, which gives the dominant kernels' average duration for the
-roofline object.  The CPU oracle is timed on a bounded sample of the headline
-workload on this host ("cpu_baseline").
+W untimed warm-up steps, then exactly K timed steps back to back, bracketed by
+torch.cuda.synchronize() (wall clock: "value" and "ms_per_step"), then K more
+attention calls each timed alone with HIP events on the stream it runs on, after a
+512 MiB cache-evicting read: their median gives the roofline object (the
+back-to-back mean is reported beside it).  The CPU oracle is timed on a bounded
+sample of the headline workload on this host's cores ("cpu_baseline").
 """
 from __future__ import annotations
 
@@ -217,7 +218,7 @@ def run_gdn(name: str, steps: int, warmup: int):
                 "ms_per_step": ms_step}
 
 
-def history_write_rate(wl, pool, reps: int = 10):
+def history_write_rate(wl, pool, reps: int = 10, warmup: int = 2):
     """KV_CACHE_WRITE throughput on the workload's first history chunk (up to 64K tokens):
     the same rows rewritten to the same slots, timed with HIP events."""
     import torch
@@ -230,7 +231,7 @@ def history_write_rate(wl, pool, reps: int = 10):
     def call():
         tl_kv_cache_write(pool, dk, dv, ds)
 
-    for _ in range(2):
+    for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     t = flushed_calls(call, reps)
@@ -343,6 +344,26 @@ def _counter_means(d: str, counter: str):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def write_bench(configs: str, steps: int = 20, warmup: int = 2):
+    """KV_CACHE_WRITE alone on each workload's first history chunk (up to 64K tokens; the
+    same rows to the same slots every call), so that a rocprofv3 run sees only identical
+    write_kernel dispatches (besides the cache-evicting reads between calls)."""
+    import torch
+    from paged_kv_attention_cache_amd import runner as R
+    from paged_kv_attention_cache_amd import workloads as W
+    out = {}
+    for name in [c.strip() for c in configs.split(",") if c.strip()]:
+        wl = W.make(name)
+        pool = R.make_pool(wl, fill_byte=None)
+        r = history_write_rate(wl, pool, reps=steps, warmup=warmup)
+        r["kv_dtype"] = wl.kv_dtype
+        out[name] = r
+        log(f"[bench] write {name}: {r['hist_write_GBps']:.0f} GB/s ({r['hist_write_hbm_frac']:.3f} of peak)")
+        del pool
+        torch.cuda.empty_cache()
+    print(json.dumps({"kv_cache_write": out}), flush=True)
+
+
 def hbm_ceiling(gib: int = 4, reps: int = 20):
     """Streaming-read ceiling of this GPU's HBM: a 4 GiB buffer read once per call with
     plain and with nontemporal 16-byte loads (libtl_stream.so), at several grid sizes,
@@ -430,37 +451,51 @@ def traffic_summary(cfg: str, fetch_dir: str, write_dir: str, copy_fetch_dir: st
     print("\n".join(lines))
 
 
-def stats_summary(d: str, configs: str, calls: str, command: str):
+def stats_summary(d: str, configs: str, warmup: str, steps: str, command: str):
     """Per-kernel durations from rocprofv3 --kernel-trace of one bench run, per workload.
 
-    The run executes the workloads in the order given, each making `calls` attention
-    calls (warm-up + timed); dispatches of the attention kernels are assigned to the
-    workloads in that order."""
+    The run executes the workloads in the order given; each makes `warmup` attention
+    calls, then `steps` back-to-back calls (the contract loop), then `steps` calls each
+    after a cache-evicting read (the calls the roofline is taken from).  Dispatches of
+    the attention kernels are assigned to the workloads and phases in that order.  The
+    history-write dispatches (write_kernel) of a decode workload's flushed write timing
+    are listed per workload as well."""
     import csv
     rows = sorted(csv.DictReader(open(_find_csv(d, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"]))
-    n = int(calls)
-    att = [r for r in rows if any(k in r["Kernel_Name"] for k in ATTN_KERNELS)]
-    mains = [i for i, r in enumerate(att) if any(k in r["Kernel_Name"] for k in
+    w, k = int(warmup), int(steps)
+    n = w + 2 * k
+    att = [r for r in rows if any(x in r["Kernel_Name"] for x in ATTN_KERNELS)]
+    mains = [i for i, r in enumerate(att) if any(x in r["Kernel_Name"] for x in
                                                  ("decode_split_kernel", "prefill_kernel", "gdn_decode_kernel"))]
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
     print(f"command: {command}\n")
-    print("Durations from the kernel trace (rocprofv3 --kernel-trace --stats), grouped by workload.\n")
-    print("| workload | kernel | calls | average us | min us | max us |")
+    print(f"Durations from the kernel trace, grouped by workload.  Per workload: {w} warm-up calls, {k} "
+          f"back-to-back calls, then {k} calls each after a 512 MiB cache-evicting read (the roofline's calls).\n")
+    print("| workload | kernel | flushed calls: average us | median us | min us | back-to-back average us |")
     print("|---|---|---|---|---|---|")
+    lists = []
     for ci, cfg in enumerate(configs.split(",")):
         blk = mains[ci * n:(ci + 1) * n]
-        if not blk:
+        if len(blk) < n:
             break
-        lo = blk[0]
         hi = mains[(ci + 1) * n] if (ci + 1) * n < len(mains) else len(att)
+        phase_start = [blk[0], blk[w], blk[w + k], hi]
         per = {}
-        for r in att[lo:hi]:
-            per.setdefault(_short_name(r["Kernel_Name"]), []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        call_total = 0.0
-        for k, v in per.items():
-            call_total += sum(v) / len(v)
-            print(f"| {cfg} | {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
-        print(f"| {cfg} | whole attention call (sum of averages) | | {call_total:.1f} | | |")
+        for ph in (1, 2):
+            for r in att[phase_start[ph]:phase_start[ph + 1]]:
+                per.setdefault(_short_name(r["Kernel_Name"]), ([], []))[ph - 1].append(dur(r))
+        tot_f = tot_b = 0.0
+        for name, (b2b, fl) in per.items():
+            tot_f += float(np.mean(fl))
+            tot_b += float(np.mean(b2b))
+            print(f"| {cfg} | {name} | {np.mean(fl):.1f} | {np.median(fl):.1f} | {min(fl):.1f} | {np.mean(b2b):.1f} |")
+            lists.append((cfg, name, b2b, fl))
+        print(f"| {cfg} | whole attention call (sum of averages) | {tot_f:.1f} | | | {tot_b:.1f} |")
+    print("\nPer-call durations (us), back-to-back calls then flushed calls:\n")
+    print("| workload | kernel | back-to-back | flushed |")
+    print("|---|---|---|---|")
+    for cfg, name, b2b, fl in lists:
+        print(f"| {cfg} | {name} | {' '.join(f'{x:.0f}' for x in b2b)} | {' '.join(f'{x:.0f}' for x in fl)} |")
 
 
 def main():
@@ -468,13 +503,16 @@ def main():
         traffic_summary(*sys.argv[2:8])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--stats-summary":
-        stats_summary(*sys.argv[2:6])
+        stats_summary(*sys.argv[2:7])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
         copy_calibration()
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--hbm-ceiling":
         hbm_ceiling()
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-bench":
+        write_bench(sys.argv[2] if len(sys.argv) > 2 else "c2,c5,c2i")
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
