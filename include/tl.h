@@ -152,6 +152,29 @@ int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_h
                          float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * PAGED_ATTENTION decode that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of tl_paged_attn_decode (the same kernels, so the same bits), without the
+ * workspace: the library keeps one static device array of TL_STATIC_SCRATCH_BYTES
+ * (64 MiB) per device it runs on, held until the process ends.  The first call on a
+ * device (with that device current) resolves the array's address and clears its
+ * header with a kernel on `stream`; every call leaves the header at zero again.
+ *   - A call whose tl_paged_attn_decode_workspace_size(...) exceeds
+ *     TL_STATIC_SCRATCH_BYTES returns TL_ERR_WORKSPACE and enqueues nothing (64 MiB
+ *     holds, e.g., 128 sequences x 64 query heads of 32K positions in fp8, or 64 x 32
+ *     of 8K in bf16).
+ *   - No hipMalloc, hipFree or other allocating call is made (TL_VALIDATE=1 aside,
+ *     whose range checks copy index arrays to host memory as for every entry).
+ *   - All calls on one device share the array: calls that overlap on one GPU (e.g.
+ *     on two streams without ordering between them) race and give wrong results.
+ */
+#define TL_STATIC_SCRATCH_BYTES (64u << 20)
+int tl_paged_attn_decode_static(const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                                const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                                int32_t batch, int32_t window, float scale, float* out, void* stream);
+
+/*
  * PAGED_ATTENTION, prefill entry ("How serving works in Tlaloc", section 1: each
  * sequence has its own right-aligned row of the token axis, pads first; a token's
  * causal length is its position + 1; section 2 blockwise bullet: online softmax over

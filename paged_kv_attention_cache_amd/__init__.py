@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.tl_paged_attn_prefill_ring.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
         L.tl_kv_gather.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
         L.tl_slot_mapping.argtypes = [vp, i32, i32, vp, i32, i32, i32, i32, vp, vp]
+        L.tl_paged_attn_decode_static.argtypes = [P, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp]
+        L.tl_paged_attn_decode_static.restype = ctypes.c_int
         L.tl_gated_delta_rule_decode.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         f64 = ctypes.c_double
         L.tl_alloc_create.argtypes = [i32, i32, f64]
@@ -201,6 +203,22 @@ def tl_paged_attn_decode(pool: KVPool, q, block_tables, seq_lens, window: int = 
     _check(lib().tl_paged_attn_decode(ctypes.byref(ps), q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks,
                                       seq_lens.data_ptr(), B, window, sc, out.data_ptr(), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tl_paged_attn_decode_static(pool: KVPool, q, block_tables, seq_lens, window: int = 0,
+                                scale: float | None = None, out=None, stream=None):
+    """PAGED_ATTENTION decode with the library's static scratch (no workspace argument;
+    the call allocates nothing): same arguments and results as tl_paged_attn_decode."""
+    import torch
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    ps = pool.c_struct()
+    sc = default_scale(D) if scale is None else scale
+    _check(lib().tl_paged_attn_decode_static(ctypes.byref(ps), q.data_ptr(), Hq, block_tables.data_ptr(),
+                                             int(block_tables.shape[1]), seq_lens.data_ptr(), B, window, sc,
+                                             out.data_ptr(), _stream(stream)))
     return out
 
 

@@ -7,9 +7,16 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "tl_internal.h"
+
+// The decode workspace of tl_paged_attn_decode_static, for callers that cannot
+// allocate: one copy on every device the library runs on, held until the process
+// ends.  Host code never uses this name as an address (on the host it is only a
+// stand-in for the symbol); the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[TL_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -275,6 +282,43 @@ int prefill_common(const char* fn, const tl_kv_pool* pool, const float* q, int32
   return ok();
 }
 
+// ------------------------------------------------- static scratch (no allocation)
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES];  // device address of `scratch` on each device, once set up
+
+__global__ __launch_bounds__(256) void zero_words_kernel(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// This device's scratch address.  On the first call on a device (with that device
+// current) the address is resolved with hipGetSymbolAddress and the workspace header
+// is cleared by a fill kernel on `s`, ordered before the caller's kernels on that
+// stream.  Later calls leave the header at zero themselves.
+int static_scratch(const char* fn, hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(TL_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices the library tracks", fn, dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (!p) return fail(TL_ERR_HIP, "%s: hipGetSymbolAddress gave no address for the static scratch", fn);
+    const int words = (int)(tl::DECODE_WS_HEADER / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, static_cast<int*>(p),
+                       words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(fn, e);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return TL_OK;
+}
+
 }  // namespace
 
 namespace tl {
@@ -343,6 +387,30 @@ int tl_paged_attn_decode(const tl_kv_pool* pool, const float* q, int32_t num_q_h
                          float* out, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common("tl_paged_attn_decode", pool, q, num_q_heads, block_tables, max_blocks, 0, seq_lens, batch,
                        window, scale, out, workspace, workspace_bytes, stream);
+}
+
+int tl_paged_attn_decode_static(const tl_kv_pool* pool, const float* q, int32_t num_q_heads,
+                                const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
+                                int32_t window, float scale, float* out, void* stream) {
+  const char* fn = "tl_paged_attn_decode_static";
+  int rc = check_pool(fn, pool);
+  if (rc) return rc;
+  if ((rc = check_group(fn, pool, num_q_heads))) return rc;
+  if (batch < 0) return fail(TL_ERR_INVALID, "%s: batch (%d) must be >= 0", fn, batch);
+  if (max_blocks <= 0) return fail(TL_ERR_INVALID, "%s: max_blocks (%d) must be > 0", fn, max_blocks);
+  if ((int64_t)max_blocks * pool->page_size >= ((int64_t)1 << 31))
+    return fail(TL_ERR_UNSUPPORTED, "%s: max_blocks * page_size must be < 2^31", fn);
+  if (batch == 0) return ok();
+  const size_t need = decode_ws_bytes(pool, batch, num_q_heads, decode_nsplit(pool, num_q_heads, max_blocks));
+  if (need > (size_t)TL_STATIC_SCRATCH_BYTES)
+    return fail(TL_ERR_WORKSPACE,
+                "%s: this call needs %zu bytes of workspace, more than the %zu bytes of static scratch per device "
+                "(pass a workspace to tl_paged_attn_decode instead)",
+                fn, need, (size_t)TL_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = static_scratch(fn, (hipStream_t)stream, &ws))) return rc;
+  return decode_common(fn, pool, q, num_q_heads, block_tables, max_blocks, 0, seq_lens, batch, window, scale, out, ws,
+                       (size_t)TL_STATIC_SCRATCH_BYTES, stream);
 }
 
 size_t tl_paged_attn_decode_ring_workspace_size(const tl_kv_pool* pool, int32_t batch, int32_t num_q_heads,
