@@ -451,6 +451,127 @@ def traffic_summary(cfg: str, fetch_dir: str, write_dir: str, copy_fetch_dir: st
     print("\n".join(lines))
 
 
+def _dispatches(d: str, suffix: str):
+    """Rows of one rocprofv3 CSV in dispatch order."""
+    import csv
+    return sorted(csv.DictReader(open(_find_csv(d, suffix))), key=lambda r: int(r["Start_Timestamp"]))
+
+
+def _counters_by_dispatch(d: str):
+    """{dispatch id: (kernel name, duration ns, {counter: value summed over instances})}, in order."""
+    out = {}
+    for r in _dispatches(d, "counter_collection.csv"):
+        k = r["Dispatch_Id"]
+        if k not in out:
+            out[k] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {})
+        c = out[k][2]
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _copy_factors(copy_fetch_dir: str, copy_write_dir: str):
+    cf = max(v[0] for v in _counter_means(copy_fetch_dir, "FETCH_SIZE").values()) * 1024
+    cw = max(v[0] for v in _counter_means(copy_write_dir, "WRITE_SIZE").values()) * 1024
+    return (1 << 30) / cf, (1 << 30) / cw, cf, cw
+
+
+def write_summary(trace_dir: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                  configs: str, warmup: str, steps: str, command: str):
+    """KV_CACHE_WRITE (write_kernel) from `bench.py --write-bench`: per workload, the
+    flushed calls' durations from the kernel trace, and HBM bytes per dispatch from
+    FETCH_SIZE / WRITE_SIZE scaled by the 1 GiB copy calibration, against the
+    algorithmic bytes of one call."""
+    from paged_kv_attention_cache_amd import accounting as A
+    from paged_kv_attention_cache_amd import workloads as W
+    w, k = int(warmup), int(steps)
+    f_fetch, f_write, cf, cw = _copy_factors(copy_fetch_dir, copy_write_dir)
+    trace = [r for r in _dispatches(trace_dir, "kernel_trace.csv") if "write_kernel" in r["Kernel_Name"]]
+    fetch = [v for v in _counters_by_dispatch(fetch_dir).values() if "write_kernel" in v[0]]
+    write = [v for v in _counters_by_dispatch(write_dir).values() if "write_kernel" in v[0]]
+    print(f"command: {command}\n")
+    print(f"calibration: a 1 GiB device copy reads {cf / 1024:.0f} KiB (FETCH_SIZE x {f_fetch:.3f}) and writes "
+          f"{cw / 1024:.0f} KiB (WRITE_SIZE x {f_write:.3f}) per dispatch\n")
+    print(f"Per workload: {w} warm-up calls, then {k} calls each after a 512 MiB cache-evicting read; durations "
+          f"are of those {k}, traffic the mean over all {w + k} dispatches.\n")
+    print("| workload | kv dtype | tokens | algorithmic bytes | median us | algorithmic GB/s | of 8 TB/s | read (scaled) | "
+          "written (scaled) | traffic / algorithmic |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    n = w + k
+    for ci, cfg in enumerate(configs.split(",")):
+        wl = W.make(cfg)
+        _, _, slots = next(wl.history_batches())
+        alg = A.write_bytes(slots, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace[ci * n + w:(ci + 1) * n]]
+        rd = np.mean([v[2]["FETCH_SIZE"] for v in fetch[ci * n:(ci + 1) * n]]) * 1024 * f_fetch
+        wr = np.mean([v[2]["WRITE_SIZE"] for v in write[ci * n:(ci + 1) * n]]) * 1024 * f_write
+        med = float(np.median(durs))
+        print(f"| {cfg} | {wl.kv_dtype} | {len(slots)} | {alg / 1e6:.1f} MB | {med:.1f} | {alg / med / 1e3:.0f} | "
+              f"{alg / med / 1e3 / HBM_PEAK_GBPS:.3f} | {rd / 1e6:.1f} MB | {wr / 1e6:.1f} MB | {(rd + wr) / alg:.3f} |")
+
+
+def mfma_summary(d: str, configs: str, warmup: str, steps: str, command: str):
+    """Prefill MFMA counters per workload: f32 MFMA flops counted by the hardware
+    (SQ_INSTS_VALU_MFMA_MOPS_F32 x 512) against the algorithmic flops (visible pairs
+    only), the MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs;
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's count is an eighth) and the
+    effective clock."""
+    from paged_kv_attention_cache_amd import accounting as A
+    from paged_kv_attention_cache_amd import workloads as W
+    per = [v for v in _counters_by_dispatch(d).values() if "prefill_kernel" in v[0]]
+    n = int(warmup) + 2 * int(steps)
+    print(f"command: {command}\n")
+    print("| workload | dispatches | algorithmic TFLOP | MFMA f32 TFLOP counted | counted / algorithmic | "
+          "duration us | algorithmic TFLOP/s | of 157.3 | MFMA busy | clock GHz |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for ci, cfg in enumerate(configs.split(",")):
+        wl = W.make(cfg)
+        alg = A.prefill_flops(wl.row_positions(), wl.num_q_heads, wl.head_dim, wl.window)
+        rows = per[ci * n:(ci + 1) * n]
+        if not rows:
+            break
+        mops = np.mean([r[2]["SQ_INSTS_VALU_MFMA_MOPS_F32"] for r in rows]) * 512
+        busy = np.mean([r[2]["SQ_VALU_MFMA_BUSY_CYCLES"] for r in rows])
+        gui = np.mean([r[2]["GRBM_GUI_ACTIVE"] for r in rows])
+        dur = np.mean([r[1] for r in rows])
+        xcd_cycles = gui / 8
+        simds = 256 * 4
+        print(f"| {cfg} | {len(rows)} | {alg / 1e12:.4f} | {mops / 1e12:.4f} | {mops / alg:.3f} | {dur / 1e3:.1f} | "
+              f"{alg / dur / 1e3:.1f} | {alg / dur / 1e3 / MFMA_F32_PEAK_TFLOPS:.3f} | "
+              f"{busy / (xcd_cycles * simds):.3f} | {xcd_cycles / dur:.2f} |")
+
+
+def hbm_summary(result_json: str, trace_dir: str, command: str):
+    """The streaming-read ceiling: `bench.py --hbm-ceiling`'s event-timed medians beside
+    the kernel trace of the same mode (stream_read_kernel dispatches of 4 GiB; the
+    512 MiB cache-evicting reads between them are listed apart)."""
+    res = json.loads(open(result_json).read().strip().splitlines()[-1])
+    rows = [r for r in _dispatches(trace_dir, "kernel_trace.csv") if "stream_read_kernel" in r["Kernel_Name"]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    big = [x for x in durs if x > 300.0]  # 4 GiB reads; the 512 MiB evicting reads take about 100 us
+    print(f"command: {command}\n")
+    print("| loads, workgroups of 256 | median GB/s (HIP events) | best GB/s | of 8 TB/s |")
+    print("|---|---|---|---|")
+    for k, v in res["hbm_stream_read"].items():
+        print(f"| {k} | {v['median_GBps']:.0f} | {v['max_GBps']:.0f} | {v['median_GBps'] / HBM_PEAK_GBPS:.3f} |")
+    if big:
+        print(f"\nKernel trace: {len(big)} dispatches of 4 GiB, {np.mean(big):.1f} us average, "
+              f"{min(big):.1f} us min ({(4 << 30) / min(big) / 1e3:.0f} GB/s at the fastest).")
+
+
+def clock_summary(d: str, kernels: str, command: str):
+    """Effective clock per dispatch (GRBM_GUI_ACTIVE summed over the 8 XCDs, divided by
+    8 and by the dispatch's duration) for the named kernels, in launch order."""
+    per = list(_counters_by_dispatch(d).values())
+    print(f"command: {command}\n")
+    print("| kernel | dispatches | duration us, in order | clock GHz, in order |")
+    print("|---|---|---|---|")
+    for name in kernels.split(","):
+        rows = [r for r in per if name in r[0]]
+        durs = " ".join(f"{r[1] / 1e3:.0f}" for r in rows)
+        ghz = " ".join(f"{r[2]['GRBM_GUI_ACTIVE'] / 8 / r[1]:.2f}" for r in rows)
+        print(f"| {_short_name(rows[0][0])} | {len(rows)} | {durs} | {ghz} |")
+
+
 def stats_summary(d: str, configs: str, warmup: str, steps: str, command: str):
     """Per-kernel durations from rocprofv3 --kernel-trace of one bench run, per workload.
 
@@ -504,6 +625,18 @@ def main():
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--stats-summary":
         stats_summary(*sys.argv[2:7])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-summary":
+        write_summary(*sys.argv[2:11])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--mfma-summary":
+        mfma_summary(*sys.argv[2:7])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--hbm-summary":
+        hbm_summary(*sys.argv[2:5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--clock-summary":
+        clock_summary(*sys.argv[2:5])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
         copy_calibration()
