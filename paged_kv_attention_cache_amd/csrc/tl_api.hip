@@ -123,7 +123,7 @@ int check_group(const char* fn, const tl_kv_pool* pool, int32_t num_q_heads) {
 }
 
 int64_t decode_nsplit(const tl_kv_pool* pool, int32_t num_q_heads, int32_t max_blocks) {
-  const int sk = tl::decode_split_keys(pool->dtype, num_q_heads / pool->num_kv_heads, pool->page_size);
+  const int sk = tl::decode_split_keys(pool->dtype, num_q_heads / pool->num_kv_heads, pool->head_dim, pool->page_size);
   const int64_t keys = (int64_t)max_blocks * pool->page_size;
   return (keys + sk - 1) / sk;
 }
@@ -137,7 +137,7 @@ int32_t ring_window(const tl_kv_pool* pool, int32_t ring_pages, int32_t window) 
 // Splits a row of a ring touches: its keys are the last ring_window() positions,
 // which span at most (w - 1) / sk + 2 splits of sk keys.
 int64_t ring_nsplit(const tl_kv_pool* pool, int32_t num_q_heads, int32_t ring_pages, int32_t window) {
-  const int sk = tl::decode_split_keys(pool->dtype, num_q_heads / pool->num_kv_heads, pool->page_size);
+  const int sk = tl::decode_split_keys(pool->dtype, num_q_heads / pool->num_kv_heads, pool->head_dim, pool->page_size);
   return (ring_window(pool, ring_pages, window) - 1) / sk + 2;
 }
 
@@ -208,7 +208,7 @@ int decode_common(const char* fn, const tl_kv_pool* pool, const float* q, int32_
   a.num_q_heads = num_q_heads; a.group = num_q_heads / pool->num_kv_heads; a.max_blocks = width;
   a.batch = batch; a.window = ring ? ring_window(pool, ring, window) : window;
   a.ring = ring;
-  a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->page_size);
+  a.split_keys = tl::decode_split_keys(pool->dtype, a.group, pool->head_dim, pool->page_size);
   a.n_split = (int)ns;
   a.fuse_merge = 0;  // chosen per kernel at launch
   a.qscale = scale * tl::LOG2E;

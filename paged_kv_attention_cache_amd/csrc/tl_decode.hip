@@ -25,6 +25,7 @@
 // - fp8: the per-(token, head) K scale multiplies the finished dot; the V scale
 //   multiplies the probability before the value product (the sum over keys is
 //   unchanged, since both are per key).
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -64,10 +65,7 @@ __device__ __forceinline__ int page_uniform(int tab, int local) { return __built
 // small; bf16 and f32 tiles at D = 128 rely on more waves per SIMD instead).  For
 // int8 at D = 128, measured on the c2 layer: 0 193 us, 1 145 us, 2 168 us (spills).
 template <int KVT, int D, int G> struct DecodePrefetch {
-#ifndef TL_DECODE_PF_I8
-#define TL_DECODE_PF_I8 1
-#endif
-  static constexpr int value = (KVT == KV_INT8 && D == 128) ? TL_DECODE_PF_I8
+  static constexpr int value = (KVT == KV_INT8 && D == 128) ? 1
                              : (kv_fp8(KVT) && D == 128 && G == 8) ? 1 : (D == 64 ? 1 : 0);
 };
 
@@ -546,21 +544,173 @@ __device__ __forceinline__ void xqueries(const float (&qraw)[8], float qscale, i
   qs[(1 * 4 + st) * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
 }
 
-#ifndef TL_DECODE_WAVES
-#define TL_DECODE_WAVES 2
-#endif
+// ---------------------------------------------- bf16 KV, D = 128, G = 4: exact bf16 split
+// The same arithmetic for a KV head with 4 query heads, one KV head per wave.  Every
+// stored K and V value is a bf16, and the f32 operand on the other side is split
+// exactly into hi + mid + lo bf16 terms.  The 4 heads' 3 terms fill 12 of a tile's 16 columns, so one column tile
+// holds them all.  Per 32-key tile (lane l, c = l % 16, g = l / 16):
+//   scores  S^T[key, col] = sum_d K[key, d] Q3[col, d] for each 16-key half over four
+//           32-wide d steps: 8 MFMAs.  Column c is term c / 4 (hi, mid, lo; 3 = zero) of
+//           head c % 4; lane (c, g) gets keys 16h + 4g + r of column c.  A butterfly
+//           over lanes c ^ 4 and c ^ 8 adds the columns c % 4 + 4t, leaving in every
+//           lane head c % 4's whole score for its 8 keys.
+//   values  O3[row, d] += sum_key P3[row, key] V[key, d], d = 8c + n in d tile n: 8
+//           MFMAs.  Row c is term c / 4 of head c % 4's probability, which lane (c, g)
+//           computed itself for exactly the keys its operand needs (k = 8g + e stands for
+//           key 16(e / 4) + 4g + e % 4, as in the score lanes).  Accumulator row 4g + r is
+//           term g of head r.
+// In score step s, k = 8g + e stands for d = 32g + 8s + e (as for G = 8): a lane's K
+// bytes are its key's d 32g .. 32g + 31, the bf16 chunks 4g .. 4g + 3, each of which is
+// the A operand of one step as loaded.
+struct X4Buf {
+  u32x4 k[2][4];      // [half][step]: key 16 * half + c, chunk 4g + step
+  uint32_t v[8][4];   // [e]: key 16(e/4) + 4g + e%4 at d 8c .. 8c + 7
+};
+
+__device__ __forceinline__ void x4load_k(X4Buf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  constexpr int NC = 128 / 8;
+  const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const XHalf x = xhalf(a, sp, k0, h);
+    const int key = clampi(x.hk0 + c, sp.lo, sp.hi);
+    const uint4* kb = reinterpret_cast<const uint4*>(a.pool.k) + (x.ph * NC + 4 * g) * S + (key & (S - 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t.k[h][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)j * S));
+  }
+}
+
+__device__ __forceinline__ void x4load_v(X4Buf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  constexpr int D = 128;
+  const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const XHalf x = xhalf(a, sp, k0, h);
+    // rows of keys hk0 + 4g + r, clamped into [lo, hi]; d 8c .. 8c + 7
+    const int rlo = sp.lo - x.hk0, rhi = sp.hi - x.hk0;
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.pool.v) + (x.ph * S + (x.hk0 & (S - 1))) * D + 8 * c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = min(max(4 * g + r, rlo), rhi);
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)row * D));
+      t.v[4 * h + r][0] = w[0]; t.v[4 * h + r][1] = w[1]; t.v[4 * h + r][2] = w[2]; t.v[4 * h + r][3] = w[3];
+    }
+  }
+}
+
+// One 32-key tile on the operands in t (each part reloaded with the next tile's once
+// used); qs: this item's Q3 operands in LDS ([d step][lane]); o: [d tile].  Lazy
+// running max as in xtile.
+template <typename Hook = NoHook>
+__device__ __forceinline__ void xtile4(const DecodeArgs& a, const Split& sp, X4Buf& t, int k0, int k_next,
+                                       const bf16x8* qs, v4f (&o)[8], float& m, float& l, Hook hook = Hook()) {
+  const int c = sp.lane & 15, g = sp.lane >> 4, term = c >> 2;
+  const bool more = k_next <= sp.k_end;
+  // ---- scores; then every lane holds head c % 4's score of keys 16h + 4g + r
+  v4f sc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v4f acc = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[h][st]), qs[st * 64 + sp.lane],
+                                                    acc, 0, 0, 0);
+    // The four columns of a head are added as a butterfly over lanes c ^ 4, then c ^ 8
+    // (within a 16-lane row the rotation by 8 is the xor): every lane of the head adds
+    // the same two numbers at each level, so all four hold bit-identical scores.  They
+    // then agree on the max, the probabilities and their hi / mid / lo split, so the
+    // three terms of one probability, taken from different lanes, add up to it exactly.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = acc[r] + __shfl_xor(acc[r], 4, 64);
+      sc[h][r] = x + ror8f(x);
+    }
+  }
+  if (more) x4load_k(t, a, sp, k_next);
+  // ---- mask, online softmax for head c % 4 over the wave's 32 keys
+  float s8[8], tmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int h = e >> 2, r = e & 3;
+    const int key = k0 + 16 * h + 4 * g + r;
+    const bool valid = key >= sp.lo && key <= sp.k_end;
+    s8[e] = valid ? sc[h][r] : -INFINITY;
+    tmax = fmaxf(tmax, s8[e]);
+  }
+  tmax = wave_xor_max(tmax, 16);
+  tmax = wave_xor_max(tmax, 32);
+  const float m_new = (m == -INFINITY || tmax > m + 8.0f) ? tmax : m;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = (m == -INFINITY) ? 1.0f : fast_exp2(m - m_use);
+  float psum = 0.0f, pt[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = fast_exp2(s8[e] - m_use);
+    psum += p;
+    float hi, mid, lo;
+    split3(p, hi, mid, lo);
+    pt[e] = term == 0 ? hi : (term == 1 ? mid : (term == 2 ? lo : 0.0f));
+  }
+  l = l * alpha + psum;
+  m = m_new;
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{bf16_pair_of(pt[0], pt[1]), bf16_pair_of(pt[2], pt[3]),
+                                                     bf16_pair_of(pt[4], pt[5]), bf16_pair_of(pt[6], pt[7])});
+  // ---- rescale: accumulator row 4g + r belongs to head r
+  if (__any(alpha != 1.0f)) {
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, r, 64);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[n][r] *= ar[r];
+  }
+  // ---- values: B operand of d tile n = V[key(8g + e)][8c + n] for e = 0..7, the n-th
+  // bf16 of each key's 8 (high or low half of word n / 2)
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) w[qd] = __builtin_amdgcn_perm(t.v[2 * qd + 1][n >> 1], t.v[2 * qd][n >> 1], sel);
+    o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]}), o[n],
+                                                   0, 0, 0);
+  }
+  if (more) x4load_v(t, a, sp, k_next);
+  hook();
+}
+
+// Q of an item as the B operand of the G = 4 score product: for d step st, lane l
+// holds column c = l % 16 at d = 32g + 8st + e: term c / 4 (hi, mid, lo, then zero) of
+// head c % 4.  Each wave builds one step st from qraw = Q[head c % 4][32g + 8st .. +7].
+__device__ __forceinline__ void xqueries4(const float (&qraw)[8], float qscale, int lane, int st, bf16x8* qs) {
+  const int term = (lane & 15) >> 2;
+  uint32_t w[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    float h0, m0, l0, h1, m1, l1;
+    split3(qraw[2 * qd] * qscale, h0, m0, l0);
+    split3(qraw[2 * qd + 1] * qscale, h1, m1, l1);
+    w[qd] = term == 0 ? bf16_pair_of(h0, h1) : (term == 1 ? bf16_pair_of(m0, m1) : (term == 2 ? bf16_pair_of(l0, l1) : 0u));
+  }
+  qs[st * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
 // Waves per workgroup; they share one split, and the split's combine waits for the
 // slowest of them.  Waves drift apart over a split (their loads are served at
 // different rates), so the register-tile paths use 2 waves on half-size splits; the
-// exact-split path builds its query operands one d step per wave, so it has 4.
-template <bool XP> struct DecodeWaves { static constexpr int value = XP ? 4 : TL_DECODE_WAVES; };
-#ifndef TL_DECODE_MIN_WAVES
-#define TL_DECODE_MIN_WAVES 2
-#endif
-// waves per SIMD the register budget is sized for (f32 tiles need twice the registers)
+// exact-split paths build their query operands one d step per wave, so they have 4.
+template <bool XP> struct DecodeWaves { static constexpr int value = XP ? 4 : 2; };
+// Workgroups per CU the register budget is sized for: 2 waves per SIMD (f32 tiles need
+// twice the registers of the others, so the f32 register-tile kernel gets 1).
 template <int KVT, bool XP> struct DecodeOcc {
-  static constexpr int value = KVT == KV_F32 ? 1 : TL_DECODE_MIN_WAVES;
+  static constexpr int value = (KVT == KV_F32 && !XP) ? 1 : 2;
 };
+// Head groups per sequence: an item covers one KV head when G = 8 (both slots of a
+// register tile hold its 8 query heads) or on the exact-split paths (one KV head per
+// wave); the register tiles at G <= 4 hold two KV heads, one per slot.
+template <int G, bool XP> struct OneKvHead { static constexpr bool value = G == 8 || XP; };
 
 // ---------------------------------------------------------------- work items
 // A work item is one split of one sequence for one head group.  Items are numbered
@@ -704,9 +854,9 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
   const int entry = RING ? (first_block + lane) % a.ring : min(first_block + lane, a.max_blocks - 1);
   op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + entry];
   if constexpr (XP) {
-    // lane (c, g) of wave w: head c % 8 of the group, d = 32g + 8w .. +7 (step w)
+    // lane (c, g) of wave w: head c % G of the group, d = 32g + 8w .. +7 (step w)
     const int c = lane & 15, g = lane >> 4;
-    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * 8 + (c & 7)) * D + 32 * g + 8 * w;
+    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * G + (c & (G - 1))) * D + 32 * g + 8 * w;
     const float4 x0 = *reinterpret_cast<const float4*>(qp);
     const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
     op.q[0] = x0.x; op.q[1] = x0.y; op.q[2] = x0.z; op.q[3] = x0.w;
@@ -848,7 +998,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int slot = lane >> 5, kg = (lane >> 2) & 7, j = lane & 3;
   const int H = a.pool.num_kv_heads;
-  const int gy = (G == 8) ? H : (H + 1) / 2;
+  const int gy = OneKvHead<G, XP>::value ? H : (H + 1) / 2;
 
   extern __shared__ int dyn[];  // [TABLE_INTS][batch]
   ItemTables tabs;
@@ -933,7 +1083,10 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   Item it = item_of<RING>(a, tabs, cur, gy);
   ItemOps<XP ? 8 : D / 8> op;
   item_ops<D, G, XP, RING>(a, it, lane, w, op);
-  if constexpr (XP) xqueries(op.q, a.qscale, lane, w, x_q);  // scores come out in log2 units
+  if constexpr (XP) {  // scores come out in log2 units
+    if constexpr (G == 4) xqueries4(op.q, a.qscale, lane, w, x_q);
+    else xqueries(op.q, a.qscale, lane, w, x_q);
+  }
 
   // In-place merge.  A split's partial states are counted one item later, when the
   // workgroup's next item reaches its combine: by then the coherent stores have long
@@ -946,8 +1099,8 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     __syncthreads();
     if (s_last[0]) {
       int hq0, nh;
-      if constexpr (G == 8) {
-        hq0 = pend_y * 8; nh = 8;
+      if constexpr (OneKvHead<G, XP>::value) {
+        hq0 = pend_y * G; nh = G;
       } else {
         hq0 = pend_y * 2 * G; nh = (pend_y * 2 + 1 < H) ? 2 * G : G;
       }
@@ -970,6 +1123,8 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     bool slot_on;
     if constexpr (G == 8) {
       kvh = it.y; qh_base = kvh * 8 + slot * 4; slot_on = true;
+    } else if constexpr (XP) {  // G = 4: the wave's 4 heads are the first slot's
+      kvh = it.y; qh_base = kvh * 4; slot_on = slot == 0;
     } else {
       kvh = it.y * 2 + slot; slot_on = kvh < H; qh_base = kvh * G;
       if (!slot_on) kvh = H - 1;  // keep addresses valid; results are discarded
@@ -993,7 +1148,44 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
 
     float m = -INFINITY, l = 0.0f;
     int k0 = k_begin + w * TK;
-    if constexpr (XP) {
+    if constexpr (XP && G == 4) {
+      float zero;  // (made inside the item loop, as below)
+      asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+      v4f ox[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) ox[n] = v4f{zero, zero, zero, zero};
+      static_assert(KVT == KV_BF16, "the G = 4 exact-split tile takes bf16 K and V");
+      X4Buf xb;
+      if (k0 <= k_end) {
+        x4load_k(xb, a, sp, k0);
+        x4load_v(xb, a, sp, k0);
+        while (k0 + STEP <= k_end) {
+          xtile4(a, sp, xb, k0, k0 + STEP, x_q, ox, m, l);
+          k0 += STEP;
+        }
+        xtile4(a, sp, xb, k0, k0 + STEP, x_q, ox, m, l, claim);
+      } else {
+        claim();
+      }
+      // ---- l and O summed over the lane groups (rows 4g + r: term g of head r); lane
+      // group 0 writes d tiles 0-3, group 1 d tiles 4-7 of head r, d = 8c + n, to LDS
+      l = wave_xor_sum(l, 16);
+      l = wave_xor_sum(l, 32);
+      const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = ox[n][r] + __shfl_xor(ox[n][r], 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          if (g == (n >> 2)) {
+            const int d = 8 * c + n;
+            c_acc[w][(d & 3) * 4 + r][d >> 2] = v;
+          }
+        }
+      if (lane < 4) { c_m[w][lane] = m; c_l[w][lane] = l; }
+    } else if constexpr (XP) {
+      static_assert(kv_fp8(KVT) && G == 8, "the G = 8 exact-split tile takes fp8 codes");
       // accumulators start from a zero made inside the item loop, so the compiler
       // does not keep 64 zero registers live (or spilled) across it
       float zero;
@@ -1138,7 +1330,10 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     if (!has_next) break;  // workgroup-uniform
     // (exact-split path: every wave is past the barrier above, so no tile reads the
     // query operands any more; the loop-top barrier publishes the new ones)
-    if constexpr (XP) xqueries(nop.q, a.qscale, lane, w, x_q);
+    if constexpr (XP) {
+      if constexpr (G == 4) xqueries4(nop.q, a.qscale, lane, w, x_q);
+      else xqueries(nop.q, a.qscale, lane, w, x_q);
+    }
     it = nit;
     op = nop;
   }
@@ -1249,32 +1444,33 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int i = 0; i < PER; ++i) dst[i] = l > 0.0f ? o[i] * inv : 0.0f;
 }
 
-// Resident workgroups of one kernel instantiation at a given dynamic LDS size (the
-// cache is per instantiation: each has its own register and LDS footprint).
+// Resident workgroups of one kernel instantiation at a given dynamic LDS size on the
+// current device, cached per (instantiation, device): each instantiation has its own
+// register and LDS footprint, and devices may differ in CU count.
+constexpr int RW_DEVICES = 64;
 template <auto kernel>
 int resident_workgroups(int threads, size_t dyn_lds) {
-  static int cached = 0;
-  static size_t cached_lds = 0;
-  if (cached == 0 || cached_lds != dyn_lds) {
-    int per_cu = 0, dev = 0, cus = 0;
+  static std::mutex mu;
+  static int cached[RW_DEVICES];
+  static size_t cached_lds[RW_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= RW_DEVICES) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0 || cached_lds[dev] != dyn_lds) {
+    int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess || per_cu <= 0)
       per_cu = 1;
-#ifdef TL_DECODE_WG_PER_CU
-    per_cu = std::min(per_cu, TL_DECODE_WG_PER_CU);
-#endif
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cached = per_cu * cus;
-    cached_lds = dyn_lds;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = per_cu * cus;
+    cached_lds[dev] = dyn_lds;
   }
-  return cached;
+  return cached[dev];
 }
 
 template <int KVT, int D, int G, bool XP, bool RING>
 hipError_t decode_launch_split_r(const DecodeArgs& a, hipStream_t s) {
   const int H = a.pool.num_kv_heads;
-  const int64_t gy = (G == 8) ? H : (H + 1) / 2;
+  const int64_t gy = OneKvHead<G, XP>::value ? H : (H + 1) / 2;
   const size_t dyn = (size_t)TABLE_INTS * a.batch * sizeof(int);
   const int64_t upper = (int64_t)a.batch * a.n_split * gy;
   constexpr int threads = 64 * DecodeWaves<XP>::value;
@@ -1298,8 +1494,9 @@ hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
 
 template <int KVT, int D, int G>
 hipError_t decode_launch_split(const DecodeArgs& a, hipStream_t s) {
-  // the exact bf16-split tile serves fp8 pools at D = 128, G = 8 with pages of >= 16
-  if constexpr (kv_fp8(KVT) && D == 128 && G == 8) {
+  // the exact bf16-split tiles serve fp8 pools at D = 128, G = 8, and bf16 pools at
+  // D = 128, G = 4, with pages of >= 16 (a 16-key half never straddles a page)
+  if constexpr ((kv_fp8(KVT) && D == 128 && G == 8) || (KVT == KV_BF16 && D == 128 && G == 4)) {
     if (a.pool.page_size >= 16) return decode_launch_split_x<KVT, D, G, true>(a, s);
   }
   return decode_launch_split_x<KVT, D, G, false>(a, s);
@@ -1325,16 +1522,13 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int decode_split_keys(int kv_dtype, int group, int page_size) {
-  (void)group;
-#ifndef TL_DECODE_SPLIT_FP8
-#define TL_DECODE_SPLIT_FP8 4096
-#endif
-#ifndef TL_DECODE_SPLIT_OTHER
-#define TL_DECODE_SPLIT_OTHER 512
-#endif
-  const int want = kv_fp8(kv_dtype) ? TL_DECODE_SPLIT_FP8 : TL_DECODE_SPLIT_OTHER;
-  return want < 64 * page_size ? want : 64 * page_size;  // a split spans at most 64 pages
+// Keys per split (measured on the c2, c2r and c5 layers): 4,096 for fp8 pools, 1,024
+// for bf16 pools on the G = 4 exact-split tile, 512 for the register tiles; a split's
+// table entries sit one per lane, so it spans at most 64 pages.
+int decode_split_keys(int kv_dtype, int group, int head_dim, int page_size) {
+  const bool x4 = kv_dtype == KV_BF16 && group == 4 && head_dim == 128 && page_size >= 16;
+  const int want = kv_fp8(kv_dtype) ? 4096 : (x4 ? 1024 : 512);
+  return want < 64 * page_size ? want : 64 * page_size;
 }
 
 // Batches larger than DECODE_BATCH_CHUNK run as consecutive launches over slices of

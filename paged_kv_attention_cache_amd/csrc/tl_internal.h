@@ -179,7 +179,7 @@ struct GdnArgs {
 hipError_t launch_write(const WriteArgs& a, int kv_dtype, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int kv_dtype, hipStream_t s);
 hipError_t launch_slot_mapping(const SlotMapArgs& a, hipStream_t s);
-int decode_split_keys(int kv_dtype, int group, int page_size);
+int decode_split_keys(int kv_dtype, int group, int head_dim, int page_size);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, hipStream_t s);
 int prefill_tokens_per_wg(int group);
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t s);

@@ -99,9 +99,13 @@ WS_HEADER = 16 + 2048 * 64 * 4
 
 def test_decode_workspace_size_formula():
     p = _pool(dtype=1, page_size=16, head_dim=128)
-    # bf16 splits are 512 keys (32 pages of 16): 128 blocks of 16 = 2048 keys -> 4 splits
+    # bf16 at G = 4 and D = 128 (the exact-split tile): splits of 1,024 keys (64 pages of
+    # 16): 128 blocks of 16 = 2048 keys -> 2 splits
     n = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p), 3, 8, 128)
-    assert n == 3 * 8 * 4 * (128 + 2) * 4 + WS_HEADER  # partial states (acc + m, l) after the header
+    assert n == 3 * 8 * 2 * (128 + 2) * 4 + WS_HEADER  # partial states (acc + m, l) after the header
+    # bf16 at G = 2 (the register tile): splits of 512 keys -> 4 splits
+    n2 = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p), 3, 4, 128)
+    assert n2 == 3 * 4 * 4 * (128 + 2) * 4 + WS_HEADER
     p8 = _pool(dtype=2, page_size=64, head_dim=128)
     n8 = tl.lib().tl_paged_attn_decode_workspace_size(ctypes.byref(p8), 2, 16, 512)  # 32768 keys / 4096
     assert n8 == 2 * 16 * 8 * 130 * 4 + WS_HEADER
@@ -151,13 +155,16 @@ def test_ring_entries_reject_bad_arguments_and_size_their_workspace():
     assert rc == tl.TL_ERR_INVALID and "ring_pages" in tl.tl_last_error()
     rc = L.tl_paged_attn_decode_ring(ctypes.byref(p), 0x8000, 8, 0, 4, 0xB000, 2, 64, f, 0xC000, 0x9000, 1 << 30, None)
     assert rc == tl.TL_ERR_INVALID and "ring_tables" in tl.tl_last_error()
-    # ring of 8 pages of 16 = 128 slots; window 100 spans at most 99 // 512 + 2 = 2 splits of 512 keys
+    # bf16 at G = 4, D = 128: splits of 1,024 keys.  A ring of 8 pages of 16 = 128 slots;
+    # window 100 spans at most 99 // 1024 + 2 = 2 splits
     n = L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 3, 8, 8, 100)
     assert n == WS_HEADER + 3 * 8 * 2 * (128 + 2) * 4
     # no window: the ring's 128 slots
     assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 3, 8, 8, 0) == n
-    # a window wider than a large ring is cut to the ring: 4096 slots -> 4095 // 512 + 2 = 9 splits
-    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 1, 8, 256, 10 ** 6) == WS_HEADER + 8 * 9 * 130 * 4
+    # a window wider than a large ring is cut to the ring: 4096 slots -> 4095 // 1024 + 2 = 5 splits
+    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 1, 8, 256, 10 ** 6) == WS_HEADER + 8 * 5 * 130 * 4
+    # at G = 2 (the register tile, 512-key splits): 4095 // 512 + 2 = 9 splits
+    assert L.tl_paged_attn_decode_ring_workspace_size(ctypes.byref(p), 1, 4, 256, 10 ** 6) == WS_HEADER + 4 * 9 * 130 * 4
     rc = L.tl_paged_attn_decode_ring(ctypes.byref(p), 0x8000, 8, 0xA000, 8, 0xB000, 3, 100, f, 0xC000, 0x9000, n - 1,
                                      None)
     assert rc == tl.TL_ERR_WORKSPACE
