@@ -381,7 +381,7 @@ def hbm_ceiling(gib: int = 4, reps: int = 20):
     stream = torch.cuda.current_stream()
     res = {}
     for nt in (0, 1):
-        for wg in (1024, 2048, 4096, 8192):
+        for wg in (1024, 2048, 4096, 8192, 32768, 65536):
             def call():
                 rc = L.tl_stream_read(buf.data_ptr(), n, sink.data_ptr(), nt, wg, stream.cuda_stream)
                 if rc != 0:
@@ -392,9 +392,27 @@ def hbm_ceiling(gib: int = 4, reps: int = 20):
             res[key] = {"median_GBps": n / (t["median_ms"] * 1e-3) / 1e9, "max_GBps": n / (t["min_ms"] * 1e-3) / 1e9,
                         "median_ms": t["median_ms"]}
             log(f"[bench] stream read {key}: {res[key]['median_GBps']:.0f} GB/s median")
+    # The decode kernels' access pattern: 4 KiB spans (one (page, head) of K or V at
+    # pages of 16 bf16 tokens) in a shuffled order, nontemporal loads.
+    L.tl_block_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_void_p]
+    nblk = n // 4096
+    order = torch.from_numpy(np.random.default_rng(11).permutation(nblk).astype(np.int32)).cuda()
+    gather = {}
+    for wg in (2048, 8192, 32768):
+        def gcall():
+            rc = L.tl_block_read(buf.data_ptr(), order.data_ptr(), nblk, sink.data_ptr(), 1, wg, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"tl_block_read: HIP error {rc}")
+        gcall()
+        t = flushed_calls(gcall, reps)
+        gather[f"nontemporal_wg{wg}"] = {"median_GBps": n / (t["median_ms"] * 1e-3) / 1e9,
+                                         "max_GBps": n / (t["min_ms"] * 1e-3) / 1e9, "median_ms": t["median_ms"]}
+        log(f"[bench] shuffled 4 KiB blocks wg{wg}: {gather[f'nontemporal_wg{wg}']['median_GBps']:.0f} GB/s median")
     best = max(res.items(), key=lambda kv: kv[1]["median_GBps"])
     print(json.dumps({"hbm_stream_read": res, "best": best[0], "best_median_GBps": best[1]["median_GBps"],
-                      "bytes_per_call": n, "calls": reps, "peak_GBps": HBM_PEAK_GBPS}), flush=True)
+                      "shuffled_4k_blocks": gather, "bytes_per_call": n, "calls": reps, "peak_GBps": HBM_PEAK_GBPS}),
+          flush=True)
 
 
 def copy_calibration(gib: int = 1, reps: int = 3):
@@ -553,6 +571,9 @@ def hbm_summary(result_json: str, trace_dir: str, command: str):
     print("|---|---|---|---|")
     for k, v in res["hbm_stream_read"].items():
         print(f"| {k} | {v['median_GBps']:.0f} | {v['max_GBps']:.0f} | {v['median_GBps'] / HBM_PEAK_GBPS:.3f} |")
+    for k, v in res.get("shuffled_4k_blocks", {}).items():
+        print(f"| shuffled 4 KiB blocks, {k} | {v['median_GBps']:.0f} | {v['max_GBps']:.0f} | "
+              f"{v['median_GBps'] / HBM_PEAK_GBPS:.3f} |")
     if big:
         print(f"\nKernel trace: {len(big)} dispatches of 4 GiB, {np.mean(big):.1f} us average, "
               f"{min(big):.1f} us min ({(4 << 30) / min(big) / 1e3:.0f} GB/s at the fastest).")

@@ -35,9 +35,47 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u4* p, int64_t u
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Blocks of 4 KiB (256 units) read in the order a list gives, as a paged decode reads
+// a (page, head) span of K or V: each workgroup takes four blocks per trip (one unit
+// per thread of each), so four loads per thread are in flight.
+template <bool NT>
+__global__ __launch_bounds__(256) void block_read_kernel(const u4* p, const int32_t* blocks, int64_t n_blocks,
+                                                         unsigned* sink) {
+  unsigned acc = 0;
+  int64_t b = (int64_t)blockIdx.x * 4;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (; b + 3 < n_blocks; b += stride) {
+    const u4 x0 = ld<NT>(p + (int64_t)blocks[b] * 256 + threadIdx.x);
+    const u4 x1 = ld<NT>(p + (int64_t)blocks[b + 1] * 256 + threadIdx.x);
+    const u4 x2 = ld<NT>(p + (int64_t)blocks[b + 2] * 256 + threadIdx.x);
+    const u4 x3 = ld<NT>(p + (int64_t)blocks[b + 3] * 256 + threadIdx.x);
+    acc ^= x0[0] ^ x0[1] ^ x0[2] ^ x0[3] ^ x1[0] ^ x1[1] ^ x1[2] ^ x1[3] ^ x2[0] ^ x2[1] ^ x2[2] ^ x2[3] ^ x3[0] ^
+           x3[1] ^ x3[2] ^ x3[3];
+  }
+  for (; b < n_blocks; ++b) {
+    const u4 x0 = ld<NT>(p + (int64_t)blocks[b] * 256 + threadIdx.x);
+    acc ^= x0[0] ^ x0[1] ^ x0[2] ^ x0[3];
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Read n_blocks blocks of 4 KiB of `src` in the order blocks[] (device int32 block
+// indices, each < bytes of src / 4096) gives.  Returns 0 or the launch's HIP error.
+int tl_block_read(const void* src, const int32_t* blocks, int64_t n_blocks, unsigned* sink, int nontemporal,
+                  int workgroups, void* stream) {
+  if (n_blocks <= 0 || workgroups <= 0) return 0;
+  const u4* p = static_cast<const u4*>(src);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    hipLaunchKernelGGL(block_read_kernel<true>, dim3((unsigned)workgroups), dim3(256), 0, s, p, blocks, n_blocks, sink);
+  else
+    hipLaunchKernelGGL(block_read_kernel<false>, dim3((unsigned)workgroups), dim3(256), 0, s, p, blocks, n_blocks, sink);
+  return (int)hipGetLastError();
+}
 
 // Read `bytes` (a multiple of 16, 16-byte aligned) of device memory at `src` once.
 // sink: one device word, written only in the unlikely case above.  Returns 0, or the
