@@ -409,9 +409,53 @@ def hbm_ceiling(gib: int = 4, reps: int = 20):
         gather[f"nontemporal_wg{wg}"] = {"median_GBps": n / (t["median_ms"] * 1e-3) / 1e9,
                                          "max_GBps": n / (t["min_ms"] * 1e-3) / 1e9, "median_ms": t["median_ms"]}
         log(f"[bench] shuffled 4 KiB blocks wg{wg}: {gather[f'nontemporal_wg{wg}']['median_GBps']:.0f} GB/s median")
+    # Bytes in flight: the same shuffled blocks on a persistent grid of 2 workgroups of
+    # 4 waves per CU (the decode kernels' shape; 60 KiB of dynamic LDS each caps it),
+    # with 4 .. 32 loads of 16 bytes per thread issued before any is used.
+    L.tl_block_read_depth.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    depth = {}
+    for u in (4, 8, 16, 32):
+        wgs = 2 * cus
+        read = (nblk // (wgs * u)) * wgs * u * 4096  # whole trips only
+
+        def dcall():
+            rc = L.tl_block_read_depth(buf.data_ptr(), order.data_ptr(), nblk, sink.data_ptr(), u, wgs, 61440,
+                                       stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"tl_block_read_depth: error {rc}")
+        dcall()
+        t = flushed_calls(dcall, reps)
+        depth[f"kib_in_flight_per_cu_{8 * u}"] = {"median_GBps": read / (t["median_ms"] * 1e-3) / 1e9,
+                                                  "max_GBps": read / (t["min_ms"] * 1e-3) / 1e9,
+                                                  "median_ms": t["median_ms"], "bytes": read}
+        log(f"[bench] in flight {8 * u} KiB per CU: {depth[f'kib_in_flight_per_cu_{8 * u}']['median_GBps']:.0f} GB/s")
+    # Reads and writes mixed: R bytes read per byte written (1 a copy; 2 and 4 as a KV
+    # write into bf16 or 1-byte pools), every byte counted once, after the same
+    # evicting read.
+    L.tl_stream_rw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    mixed = {}
+    for ratio in (1, 2, 4):
+        out = (n // (ratio + 1)) // 4096 * 4096
+        for ntl, nts in ((0, 0), (1, 0), (0, 1)):
+            for wg in (2048, 8192):
+                def rcall():
+                    rc = L.tl_stream_rw(buf.data_ptr(), buf.data_ptr() + ratio * out, out, ratio, ntl, nts, wg,
+                                        stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"tl_stream_rw: error {rc}")
+                rcall()
+                t = flushed_calls(rcall, reps)
+                key = f"read{ratio}_write1_{'nt' if ntl else 'plain'}loads_{'nt' if nts else 'plain'}stores_wg{wg}"
+                mixed[key] = {"median_GBps": (ratio + 1) * out / (t["median_ms"] * 1e-3) / 1e9,
+                              "max_GBps": (ratio + 1) * out / (t["min_ms"] * 1e-3) / 1e9, "median_ms": t["median_ms"]}
+                log(f"[bench] {key}: {mixed[key]['median_GBps']:.0f} GB/s median")
     best = max(res.items(), key=lambda kv: kv[1]["median_GBps"])
     print(json.dumps({"hbm_stream_read": res, "best": best[0], "best_median_GBps": best[1]["median_GBps"],
-                      "shuffled_4k_blocks": gather, "bytes_per_call": n, "calls": reps, "peak_GBps": HBM_PEAK_GBPS}),
+                      "shuffled_4k_blocks": gather, "in_flight_per_cu": depth, "read_write": mixed,
+                      "bytes_per_call": n, "calls": reps, "peak_GBps": HBM_PEAK_GBPS}),
           flush=True)
 
 
@@ -574,6 +618,13 @@ def hbm_summary(result_json: str, trace_dir: str, command: str):
     for k, v in res.get("shuffled_4k_blocks", {}).items():
         print(f"| shuffled 4 KiB blocks, {k} | {v['median_GBps']:.0f} | {v['max_GBps']:.0f} | "
               f"{v['median_GBps'] / HBM_PEAK_GBPS:.3f} |")
+    for k, v in res.get("read_write", {}).items():
+        print(f"| {k.replace('_', ' ')} | {v['median_GBps']:.0f} | {v['max_GBps']:.0f} | "
+              f"{v['median_GBps'] / HBM_PEAK_GBPS:.3f} |")
+    for k, v in res.get("in_flight_per_cu", {}).items():
+        kib = k.rsplit("_", 1)[1]
+        print(f"| shuffled 4 KiB blocks, 2 workgroups per CU, {kib} KiB in flight per CU | {v['median_GBps']:.0f} | "
+              f"{v['max_GBps']:.0f} | {v['median_GBps'] / HBM_PEAK_GBPS:.3f} |")
     if big:
         print(f"\nKernel trace: {len(big)} dispatches of 4 GiB, {np.mean(big):.1f} us average, "
               f"{min(big):.1f} us min ({(4 << 30) / min(big) / 1e3:.0f} GB/s at the fastest).")
