@@ -42,11 +42,14 @@ KERNEL_SOURCES = ("tl_decode.hip", "tl_prefill.hip", "tl_write.hip", "tl_gdn.hip
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources of the measured kernels (the traffic record is valid while it matches)."""
+    """Hash of the sources of the measured kernels and of the flags they are built with
+    (the traffic record is valid while it matches)."""
+    from paged_kv_attention_cache_amd import _build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_attention_cache_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(_build.HIP_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,9 +16,14 @@ STREAM_SOURCE = "tl_stream.hip"  # measurement support: built as libtl_stream.so
 STREAM_LIB = os.path.join(HERE, "libtl_stream.so")
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
+# The atomic optimizer off: it turns a one-lane atomic whose result is read later (the
+# decode kernels' work claim, issued a tile before the claimed number is needed) into
+# a wave-wide form that reads the result at once, so the round trip was waited on in
+# place.  Every atomic in these kernels is issued by one lane.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -607,6 +607,10 @@ __device__ __forceinline__ void xtile4(const DecodeArgs& a, const Split& sp, X4B
                                        const bf16x8* qs, v4f (&o)[8], float& m, float& l, Hook hook = Hook()) {
   const int c = sp.lane & 15, g = sp.lane >> 4, term = c >> 2;
   const bool more = k_next <= sp.k_end;
+  // work for later (the next item's claim) goes out first, so its round trip overlaps
+  // this tile's arithmetic (measured: c2 -1%; at the end of the G = 8 tile instead,
+  // where the start cost c5 5%)
+  hook();
   // ---- scores; then every lane holds head c % 4's score of keys 16h + 4g + r
   v4f sc[2];
 #pragma unroll
@@ -678,7 +682,6 @@ __device__ __forceinline__ void xtile4(const DecodeArgs& a, const Split& sp, X4B
                                                    0, 0, 0);
   }
   if (more) x4load_v(t, a, sp, k_next);
-  hook();
 }
 
 // Q of an item as the B operand of the G = 4 score product: for d step st, lane l
@@ -979,10 +982,10 @@ __device__ __forceinline__ void workgroup_done(const DecodeArgs& a, int tid) {
 // Persistent workgroups of NWD waves.  For each claimed item, wave w takes the
 // split's tiles w, w + NWD, ... with its own softmax state; the NWD states are then
 // combined through LDS in wave order, so the result depends on the split alone, not
-// on which workgroup ran it or when.  The next item number is claimed as wave 0
-// starts its last tile of the current item (so an item goes to a workgroup only when
-// that workgroup is nearly free: longest-processing-time-first scheduling), and the
-// next item's table entries and queries load while the current item is combined.
+// on which workgroup ran it or when.  The next item number is claimed during wave
+// 0's last tile of the current item (so an item goes to a workgroup only when that
+// workgroup is nearly free: longest-processing-time-first scheduling), and the next
+// item's table entries and queries load while the current item is combined.
 template <int KVT, int D, int G, bool XP, bool RING>
 __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::value)) void decode_split_kernel(
     DecodeArgs a) {
@@ -1113,10 +1116,11 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   for (;;) {
     __syncthreads();  // the previous item's combine is done everywhere
     int claimed = 0;
-    // The next item is claimed when wave 0 starts its last tile of this one, so items
-    // go to workgroups in the order they become free (longest first), and the atomic's
-    // latency hides behind that tile.
-    auto claim = [&]() { if (tid == 0) claimed = n_wg + atomicAdd(a.ws_ctrl, 1); };
+    // The next item is claimed during wave 0's last tile of this one (at its start on
+    // the register and G = 4 tiles, at its end on the G = 8 tile), so items go to
+    // workgroups in the order they become free (longest first).  The count is read
+    // only at the combine, so the add's round trip overlaps the rest of that tile.
+    auto claim = [&]() { if (tid == 0) claimed = atomicAdd(a.ws_ctrl, 1); };
 
     // ---- this item
     int kvh, qh_base;
@@ -1169,6 +1173,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       }
       // ---- l and O summed over the lane groups (rows 4g + r: term g of head r); lane
       // group 0 writes d tiles 0-3, group 1 d tiles 4-7 of head r, d = 8c + n, to LDS
+      // (value (d / 32) * 4 + r, column d % 32)
       l = wave_xor_sum(l, 16);
       l = wave_xor_sum(l, 32);
       const int c = lane & 15, g = lane >> 4;
@@ -1180,7 +1185,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
           v += __shfl_xor(v, 32, 64);
           if (g == (n >> 2)) {
             const int d = 8 * c + n;
-            c_acc[w][(d & 3) * 4 + r][d >> 2] = v;
+            c_acc[w][(d >> 5) * 4 + r][d & 31] = v;
           }
         }
       if (lane < 4) { c_m[w][lane] = m; c_l[w][lane] = l; }
@@ -1274,7 +1279,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       if (kg == 0) { c_m[w][slot * 4 + j] = m; c_l[w][slot * 4 + j] = l; }
     }
     if (FUSE && pend_b >= 0) __builtin_amdgcn_s_waitcnt(0);  // the previous item's partial stores have completed
-    if (tid == 0) s_claim[0] = claimed;
+    if (tid == 0) s_claim[0] = n_wg + claimed;
     __syncthreads();
     // the next item's table entries and queries load while this one is combined
     // (a claim is n_wg + a counter that starts at zero; any other value, from a
@@ -1293,7 +1298,11 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     }
 
     // ---- combine in wave order: value v = i*4 + r of this lane is head slot*4 + r,
-    // d = (lane % 32) * NT + i; wave w finishes the values v with v % NWD == w.
+    // d = (lane % 32) * NT + i, except on the G = 4 exact-split tile, where
+    // d = 32 i + lane % 32: there 32 lanes store a whole 128-byte line of a partial
+    // state at once (coherent stores write through to memory, and a line stored in
+    // pieces is written as several).  (On the G = 8 tile the same layout cost spilled
+    // registers; it keeps the first.)  Wave w finishes the values v with v % NWD == w.
     const bool single = (ss.s_first == ss.s_last);
     const int d_base = (lane & 31) * NT;
 #pragma unroll
@@ -1313,7 +1322,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
         lsum += wt * c_l[u][h];
         acc += wt * c_acc[u][v][lane];
       }
-      const int hq = qh_base + r, d = d_base + i;
+      const int hq = qh_base + r, d = (XP && G == 4) ? 32 * i + (lane & 31) : d_base + i;
       if (single) {
         a.out[((int64_t)it.b * a.num_q_heads + hq) * D + d] = lsum > 0.0f ? acc * (1.0f / lsum) : 0.0f;
       } else {
