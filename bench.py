@@ -180,13 +180,18 @@ def run_config(name: str, steps: int, warmup: int):
         step.run()
     torch.cuda.synchronize()
     ms_step_eager, attn_back_to_back = timed_steps(step.write, step.attend, steps)
-    ms_step = ms_step_eager
+    ms_step, step_mode = ms_step_eager, "eager"
     if wl.kind == "decode":  # launch-bound: the step runs as one replayed graph
-        graph = capture_step(step)
-        for _ in range(warmup):
-            graph.replay()
-        ms_step = graph_steps(graph, steps)
-        del graph
+        try:
+            graph = capture_step(step)
+            for _ in range(warmup):
+                graph.replay()
+            ms_step, step_mode = graph_steps(graph, steps), "graph"
+            del graph
+        except RuntimeError as e:  # reported, and the eager steps stand
+            log(f"[bench] {name}: graph capture not used ({e}); eager steps")
+            step.run()
+            torch.cuda.synchronize()
     attn = flushed_calls(step.attend, steps)
     attn_ms = attn["median_ms"]
 
@@ -198,7 +203,7 @@ def run_config(name: str, steps: int, warmup: int):
         wr_bytes = A.write_bytes(step.slots.cpu().numpy(), wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
         res = {
             "workload": wl.name, "kind": "decode", "batch": wl.batch, "kv_dtype": wl.kv_dtype,
-            "ms_per_step": ms_step, "ms_per_step_eager": ms_step_eager, "attn_ms": attn_ms,
+            "ms_per_step": ms_step, "ms_per_step_eager": ms_step_eager, "step_mode": step_mode, "attn_ms": attn_ms,
             "attn_ms_min": attn["min_ms"], "attn_ms_back_to_back": attn_back_to_back,
             "step_GBps": (attn_bytes + wr_bytes) / (ms_step * 1e-3) / 1e9,
             "attn_GBps": attn_bytes / (attn_ms * 1e-3) / 1e9,
@@ -820,7 +825,7 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "step": ("one captured HIP graph per step: the step's KV write, then its decode call"
-                 if head["kind"] == "decode" else "the step's KV write, then its attention call, launched eagerly"),
+                 if head.get("step_mode") == "graph" else "the step's KV write, then its attention call, launched eagerly"),
         "dtype": "f32", "data": "synthetic",
         "config": ({"workload": head_wl.name, "batch": head_wl.batch, "num_heads": head_wl.num_heads,
                     "head_dim": head_wl.head_dim, "num_slots": head_wl.num_slots, "parallelism": "none"}
