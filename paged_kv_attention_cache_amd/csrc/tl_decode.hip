@@ -700,6 +700,254 @@ __device__ __forceinline__ void xqueries4(const float (&qraw)[8], float qscale, 
   qs[st * 64 + lane] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
 }
 
+// ------------------------------------- int8 KV, D = 128, G = 4: integer matrix cores
+// The stored int8 codes are the operands of v_mfma_i32_16x16x64_i8 as loaded.  The f32
+// operand on the other side (the scaled queries; a head's probabilities times the V
+// scales) is written as a power of two and four 7-bit integer limbs:
+//   y = sign * 2^(E - 6) * (c0 + c1 2^-7 + c2 2^-14 + c3 2^-21),  c0 < 64, c1..c3 < 128,
+// where 2^E bounds |y| over a row (a query head over d; a head's tile of probabilities)
+// and c0..c3 are the bits of the integer truncation of |y| 2^(27 - E), which drops less
+// than 2^(E - 27) per value.  Both products are then exact integer sums: at most
+// 128 * 127 * 127 (scores) or 64 * 127 * 127 (values), below 2^24, so they convert to
+// f32 exactly, and each limb's sum is scaled by its power of two.  One 64-key tile per
+// wave (lane l, c = l % 16, g = l / 16, t = c / 4, head h = c % 4):
+//   scores  for each 16-key quarter qr: S[key, col] = sum_d K[key, d] Ql[col, d] over two
+//           64-wide d steps (8 MFMAs per tile).  Column c is limb t of head h; lane (c, g)
+//           gets keys 16qr + 4g + r and weights its sums by 2^(e_h - 6 - 7t).  A
+//           reduce-scatter over the head's four limb lanes (c ^ 4, then c ^ 8) leaves in
+//           lane (c, g) the whole score of the keys of quarter t, 16t + 4g + r: each lane
+//           runs the softmax on its own 4 keys, and each key's score is summed in one lane.
+//   values  Ol[row, d] = sum_key Pl[row, key] V[key, d], d = 8c + n for d tile n (8
+//           MFMAs).  Row c is limb t of head h's p * v_scale over the lane group's 16 keys
+//           (k = 16g + 4qr + r stands for key 16qr + 4g + r): the lane owning quarter qr
+//           cuts its 4 keys into 4 limbs, and a transpose over the four limb lanes hands
+//           limb t of every quarter to lane t.  Result row 4g + r (limb g of head r) is
+//           weighted by 2^(E_r - 6 - 7g) and added to the f32 accumulator, so the sum
+//           over lane groups at the end adds the limbs.
+// In score step s, k = 16g + j stands for d = 16(4s + g) + j: a lane's K chunk 4s + g is
+// its A operand as loaded.  V rows are loaded 8 bytes (d 8c .. 8c + 7) per key; the B
+// operand of d tile n takes byte n of each of the lane's 16 keys, a 4 x 4 byte transpose
+// per quarter and half row.  Codes of keys outside [lo, hi] are read from the same
+// page (an int8 code is never NaN) and multiplied by zero limbs or masked; their scales
+// are read from a key inside, so that they are finite.
+struct IBuf {
+  u32x4 k[4][2];  // [quarter][step]: key 16 * quarter + c, chunk 4 * step + g
+  u32x2 v[4][4];  // [quarter][r]: key 16 * quarter + 4g + r at d 8c .. 8c + 7
+  v4f ks, vs;     // scales of keys 16t + 4g .. +3
+};
+
+// (xhalf of quarter qr: the 16-key group from k0 + 16 qr, clamped into [lo, hi])
+__device__ __forceinline__ void iload_k(IBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  constexpr int NC = 128 / 16;
+  const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
+#pragma unroll
+  for (int qr = 0; qr < 4; ++qr) {
+    const XHalf x = xhalf(a, sp, k0, qr);
+    const uint4* kb = reinterpret_cast<const uint4*>(a.pool.k) + x.ph * NC * S + (x.hk0 & (S - 1)) + (g * S + c);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      t.k[qr][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)4 * s * S));
+  }
+}
+__device__ __forceinline__ void iload_v(IBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
+  constexpr int D = 128;
+  const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
+#pragma unroll
+  for (int qr = 0; qr < 4; ++qr) {
+    const XHalf x = xhalf(a, sp, k0, qr);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(a.pool.v) + (x.ph * S + (x.hk0 & (S - 1))) * D +
+                              (4 * g * D + 8 * c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t.v[qr][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + r * D));
+  }
+}
+__device__ __forceinline__ void iload_scales(IBuf& t, const DecodeArgs& a, const Split& sp, int k0, bool kside) {
+  const int S = a.pool.page_size, sh = a.pool.page_shift, c = sp.lane & 15, g = sp.lane >> 4;
+  const int g0 = clampi(k0 + 16 * (c >> 2) + 4 * g, sp.lo & ~3, sp.hi & ~3);
+  const int page = page_of_lane(sp.tab, clampi((g0 >> sh) - sp.first_block, 0, 63));
+  const int64_t si = ((int64_t)page * a.pool.num_kv_heads + sp.kvh) * S + (g0 & (S - 1));
+  if (kside) t.ks = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.k_scale + si));
+  else t.vs = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.v_scale + si));
+}
+
+// o[i] = byte i of s0, s1, s2, s3 (a 4 x 4 byte transpose)
+__device__ __forceinline__ void transpose4x4(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, uint32_t (&o)[4]) {
+  const uint32_t u0 = __builtin_amdgcn_perm(s1, s0, 0x05010400u);  // s0.0 s1.0 s0.1 s1.1
+  const uint32_t u1 = __builtin_amdgcn_perm(s1, s0, 0x07030602u);  // s0.2 s1.2 s0.3 s1.3
+  const uint32_t u2 = __builtin_amdgcn_perm(s3, s2, 0x05010400u);
+  const uint32_t u3 = __builtin_amdgcn_perm(s3, s2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(u2, u0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(u2, u0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(u3, u1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
+}
+
+// least E with |x| < 2^E (x != 0)
+__device__ __forceinline__ int bound_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
+// limb t (0..3) of the integer n = trunc(|y| 2^(27 - E)) < 2^27
+__device__ __forceinline__ uint32_t limb_of(uint32_t n, int t) { return (n >> (21 - 7 * t)) & 127u; }
+
+// Q of an item as the B operand of the int8 score product: for d step s, lane (c, g)
+// holds limb t of head h's scaled query at d = 16(4s + g) + j, j = 0..15, as signed
+// bytes, from qraw[16s + j] = Q[h][16(4s + g) + j].  Every wave finds the head's bound
+// (the lanes (c, g) of one c hold all 128 d of the head between them) and returns the
+// lane's score weight 2^(e_h - 6 - 7t); waves 0 and 1 store steps 0 and 1.
+__device__ __forceinline__ float iqueries(const float (&qraw)[32], float qscale, int lane, int w, u32x4* qs) {
+  const int t = (lane & 15) >> 2;
+  float y[32], mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    y[i] = qraw[i] * qscale;
+    mx = fmaxf(mx, fabsf(y[i]));
+  }
+  mx = wave_xor_max(mx, 16);
+  mx = wave_xor_max(mx, 32);
+  const int e = mx > 0.0f ? bound_exp(mx) : 0;  // a zero head has zero limbs
+  if (w < 2) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float v = w == 0 ? y[4 * qd + b] : y[16 + 4 * qd + b];
+        const uint32_t c = limb_of((uint32_t)__builtin_ldexpf(fabsf(v), 27 - e), t);
+        x |= ((v < 0.0f ? 0u - c : c) & 255u) << (8 * b);
+      }
+      wd[qd] = x;
+    }
+    qs[w * 64 + lane] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+  }
+  return __builtin_ldexpf(1.0f, e - 6 - 7 * t);
+}
+
+// One 64-key tile on the operands in t (each part reloaded with the next tile's once
+// used); qs: the item's Q limb operands in LDS ([d step][lane]); wq: this lane's score
+// weight; o: [d tile].  Lazy running max as in xtile.  l is this lane's part: the item's
+// sum runs over the head's 16 lanes.
+template <typename Hook = NoHook>
+__device__ __forceinline__ void itile(const DecodeArgs& a, const Split& sp, IBuf& t, int k0, int k_next,
+                                      const u32x4* qs, float wq, v4f (&o)[8], float& m, float& l,
+                                      Hook hook = Hook()) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const int c = sp.lane & 15, g = sp.lane >> 4, term = c >> 2;
+  const bool b0 = term & 1, b1 = term & 2;
+  const bool more = k_next <= sp.k_end;
+  hook();  // (as in xtile4)
+  // ---- scores: limb sums of keys 16qr + 4g + r, weighted
+  const i32x4 q0 = __builtin_bit_cast(i32x4, qs[sp.lane]), q1 = __builtin_bit_cast(i32x4, qs[64 + sp.lane]);
+  float sw[4][4];
+#pragma unroll
+  for (int qr = 0; qr < 4; ++qr) {
+    i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, t.k[qr][0]), q0, i32x4{0, 0, 0, 0},
+                                                       0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, t.k[qr][1]), q1, acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sw[qr][r] = (float)acc[r] * wq;
+  }
+  if (more) iload_k(t, a, sp, k_next);
+  // reduce-scatter over limb lanes: with lane c ^ 4 keep the quarters of parity t % 2,
+  // then with lane c ^ 8 keep quarter t
+  float s4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float hv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float keep = b0 ? sw[2 * j + 1][r] : sw[2 * j][r];
+      const float send = b0 ? sw[2 * j][r] : sw[2 * j + 1][r];
+      hv[j] = keep + __shfl_xor(send, 4, 64);
+    }
+    const float keep = b1 ? hv[1] : hv[0], send = b1 ? hv[0] : hv[1];
+    s4[r] = (keep + ror8f(send)) * t.ks[r];
+  }
+  if (more) iload_scales(t, a, sp, k_next, true);
+  // ---- mask, online softmax for head h over the keys 16t + 4g + r
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int key = k0 + 16 * term + 4 * g + r;
+    s4[r] = (key >= sp.lo && key <= sp.k_end) ? s4[r] : -INFINITY;
+    tmax = fmaxf(tmax, s4[r]);
+  }
+  tmax = wave_xor_max(tmax, 4);
+  tmax = fmaxf(tmax, ror8f(tmax));
+  tmax = wave_xor_max(tmax, 16);
+  tmax = wave_xor_max(tmax, 32);
+  const float m_new = (m == -INFINITY || tmax > m + 8.0f) ? tmax : m;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = (m == -INFINITY) ? 1.0f : fast_exp2(m - m_use);
+  float psum = 0.0f, pmax = 0.0f, pv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = fast_exp2(s4[r] - m_use);
+    psum += p;
+    pv[r] = p * t.vs[r];
+    pmax = fmaxf(pmax, pv[r]);
+  }
+  l = l * alpha + psum;
+  m = m_new;
+  if (more) iload_scales(t, a, sp, k_next, false);
+  pmax = wave_xor_max(pmax, 4);
+  pmax = fmaxf(pmax, ror8f(pmax));
+  pmax = wave_xor_max(pmax, 16);
+  pmax = wave_xor_max(pmax, 32);
+  const int E = pmax > 0.0f ? bound_exp(pmax) : 0;
+  // limbs of this lane's 4 keys: dw[u] = limb u of keys r = 0..3 (byte r), for lane u
+  uint32_t n4[4], dw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) n4[r] = (uint32_t)__builtin_ldexpf(pv[r], 27 - E);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    dw[u] = limb_of(n4[0], u) | (limb_of(n4[1], u) << 8) | (limb_of(n4[2], u) << 16) | (limb_of(n4[3], u) << 24);
+  // transpose over limb lanes: lane t ends with limb t of every quarter's keys
+  uint32_t own[2], rcv[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // columns t % 2 + 2k: rows t and t ^ 1
+    own[k] = b0 ? dw[1 + 2 * k] : dw[2 * k];
+    const uint32_t send = b0 ? dw[2 * k] : dw[1 + 2 * k];
+    rcv[k] = (uint32_t)__shfl_xor((int)send, 4, 64);
+  }
+  const uint32_t m_t = b1 ? own[1] : own[0], m_t1 = b1 ? rcv[1] : rcv[0];   // rows t, t ^ 1
+  const uint32_t m_t2 = ror8(b1 ? own[0] : own[1]), m_t3 = ror8(b1 ? rcv[0] : rcv[1]);  // rows t ^ 2, t ^ 3
+  uint32_t pw[4];
+#pragma unroll
+  for (int qr = 0; qr < 4; ++qr) {  // dword qr = row qr = row t ^ (qr ^ t)
+    const bool x0 = ((qr & 1) != 0) != b0, x1 = ((qr & 2) != 0) != b1;
+    pw[qr] = x1 ? (x0 ? m_t3 : m_t2) : (x0 ? m_t1 : m_t);
+  }
+  const i32x4 pa = i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+  // ---- rescale: accumulator row 4g + r belongs to head r; its limb g weighs 2^(E_r - 6 - 7g)
+  if (__any(alpha != 1.0f)) {
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, r, 64);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[n][r] *= ar[r];
+  }
+  float wv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) wv[r] = __builtin_ldexpf(1.0f, __builtin_amdgcn_readlane(E, r) - 6 - 7 * g);
+  // ---- values: B operand of d tile n = 4hw + i: byte n of each key's 8
+  uint32_t vt[2][4][4];  // [hw][quarter][i]
+#pragma unroll
+  for (int hw = 0; hw < 2; ++hw)
+#pragma unroll
+    for (int qr = 0; qr < 4; ++qr)
+      transpose4x4(t.v[qr][0][hw], t.v[qr][1][hw], t.v[qr][2][hw], t.v[qr][3][hw], vt[hw][qr]);
+  if (more) iload_v(t, a, sp, k_next);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int hw = n >> 2, i = n & 3;
+    const i32x4 vb = i32x4{(int)vt[hw][0][i], (int)vt[hw][1][i], (int)vt[hw][2][i], (int)vt[hw][3][i]};
+    const i32x4 r32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vb, i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[n][r] += (float)r32[r] * wv[r];
+  }
+}
+
 // Waves per workgroup; they share one split, and the split's combine waits for the
 // slowest of them.  Waves drift apart over a split (their loads are served at
 // different rates), so the register-tile paths use 2 waves on half-size splits; the
@@ -850,13 +1098,29 @@ __device__ __forceinline__ void item_heads(const DecodeArgs& a, int y, int lane,
   }
 }
 
-template <int D, int G, bool XP, bool RING>
+// query registers per lane: register tiles D / 8, the bf16-split tiles 8 (one d step
+// per wave), the int8 tile 32 (both d steps: every wave needs the head's bound)
+template <int D, bool XP, bool XI> struct ItemQ { static constexpr int value = XI ? 32 : (XP ? 8 : D / 8); };
+
+template <int D, int G, bool XP, bool XI, bool RING>
 __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, int lane, int w,
-                                         ItemOps<XP ? 8 : D / 8>& op) {
+                                         ItemOps<ItemQ<D, XP, XI>::value>& op) {
   const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
   const int entry = RING ? (first_block + lane) % a.ring : min(first_block + lane, a.max_blocks - 1);
   op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + entry];
-  if constexpr (XP) {
+  if constexpr (XI) {
+    // lane (c, g): head c % 4 of the group, d = 16g .. 16g + 15 and 64 + 16g .. + 15
+    const int c = lane & 15, g = lane >> 4;
+    const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * G + (c & (G - 1))) * D + 16 * g;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 x = *reinterpret_cast<const float4*>(qp + 64 * s + 4 * u);
+        op.q[16 * s + 4 * u] = x.x; op.q[16 * s + 4 * u + 1] = x.y;
+        op.q[16 * s + 4 * u + 2] = x.z; op.q[16 * s + 4 * u + 3] = x.w;
+      }
+  } else if constexpr (XP) {
     // lane (c, g) of wave w: head c % G of the group, d = 32g + 8w .. +7 (step w)
     const int c = lane & 15, g = lane >> 4;
     const float* qp = a.q + ((int64_t)it.b * a.num_q_heads + it.y * G + (c & (G - 1))) * D + 32 * g + 8 * w;
@@ -994,7 +1258,11 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
   using GE = Geo<KVT, D>;
   constexpr int NT = GE::NT;
   constexpr int PF = DecodePrefetch<KVT, D, G>::value;
-  constexpr int STEP = NWD * TK;
+  // the int8 tile (exact-split path, int8 codes) takes 64 keys per wave, the others 32
+  constexpr bool XI = XP && KVT == KV_INT8;
+  constexpr int TKW = XI ? 64 : TK;
+  constexpr int STEP = NWD * TKW;
+  constexpr int NQR = ItemQ<D, XP, XI>::value;
   // In-place merge on the exact-split path only (measured: it saves the merge launch
   // there, while the register-tile kernels lose more than that to it)
   constexpr bool FUSE = XP;
@@ -1084,10 +1352,12 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     return;
   }
   Item it = item_of<RING>(a, tabs, cur, gy);
-  ItemOps<XP ? 8 : D / 8> op;
-  item_ops<D, G, XP, RING>(a, it, lane, w, op);
+  ItemOps<NQR> op;
+  item_ops<D, G, XP, XI, RING>(a, it, lane, w, op);
+  float wq = 0.0f;  // int8 tile: this lane's score weight for the item
   if constexpr (XP) {  // scores come out in log2 units
-    if constexpr (G == 4) xqueries4(op.q, a.qscale, lane, w, x_q);
+    if constexpr (XI) wq = iqueries(op.q, a.qscale, lane, w, reinterpret_cast<u32x4*>(x_q));
+    else if constexpr (G == 4) xqueries4(op.q, a.qscale, lane, w, x_q);
     else xqueries(op.q, a.qscale, lane, w, x_q);
   }
 
@@ -1151,29 +1421,52 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     sp.tab = clampi(op.tab, 0, a.pool.num_pages - 1);
 
     float m = -INFINITY, l = 0.0f;
-    int k0 = k_begin + w * TK;
+    int k0 = k_begin + w * TKW;
     if constexpr (XP && G == 4) {
       float zero;  // (made inside the item loop, as below)
       asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
       v4f ox[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) ox[n] = v4f{zero, zero, zero, zero};
-      static_assert(KVT == KV_BF16, "the G = 4 exact-split tile takes bf16 K and V");
-      X4Buf xb;
-      if (k0 <= k_end) {
-        x4load_k(xb, a, sp, k0);
-        x4load_v(xb, a, sp, k0);
-        while (k0 + STEP <= k_end) {
-          xtile4(a, sp, xb, k0, k0 + STEP, x_q, ox, m, l);
-          k0 += STEP;
+      static_assert(KVT == KV_BF16 || KVT == KV_INT8, "the G = 4 exact-split tiles take bf16 or int8 K and V");
+      if constexpr (XI) {
+        const u32x4* qi = reinterpret_cast<const u32x4*>(x_q);
+        IBuf ib;
+        if (k0 <= k_end) {
+          iload_k(ib, a, sp, k0);
+          iload_scales(ib, a, sp, k0, true);
+          iload_scales(ib, a, sp, k0, false);
+          iload_v(ib, a, sp, k0);
+          while (k0 + STEP <= k_end) {
+            itile(a, sp, ib, k0, k0 + STEP, qi, wq, ox, m, l);
+            k0 += STEP;
+          }
+          itile(a, sp, ib, k0, k0 + STEP, qi, wq, ox, m, l, claim);
+        } else {
+          claim();
         }
-        xtile4(a, sp, xb, k0, k0 + STEP, x_q, ox, m, l, claim);
       } else {
-        claim();
+        X4Buf xb;
+        if (k0 <= k_end) {
+          x4load_k(xb, a, sp, k0);
+          x4load_v(xb, a, sp, k0);
+          while (k0 + STEP <= k_end) {
+            xtile4(a, sp, xb, k0, k0 + STEP, x_q, ox, m, l);
+            k0 += STEP;
+          }
+          xtile4(a, sp, xb, k0, k0 + STEP, x_q, ox, m, l, claim);
+        } else {
+          claim();
+        }
       }
       // ---- l and O summed over the lane groups (rows 4g + r: term g of head r); lane
       // group 0 writes d tiles 0-3, group 1 d tiles 4-7 of head r, d = 8c + n, to LDS
-      // (value (d / 32) * 4 + r, column d % 32)
+      // (value (d / 32) * 4 + r, column d % 32).  (On the int8 tile the lanes of a head
+      // also hold different keys.)
+      if constexpr (XI) {
+        l = wave_xor_sum(l, 4);
+        l += ror8f(l);
+      }
       l = wave_xor_sum(l, 16);
       l = wave_xor_sum(l, 32);
       const int c = lane & 15, g = lane >> 4;
@@ -1288,10 +1581,10 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     const int nxt = uni(s_claim[0]);
     const bool has_next = nxt >= n_wg && nxt < n_items;
     Item nit = it;
-    ItemOps<XP ? 8 : D / 8> nop;
+    ItemOps<NQR> nop;
     if (has_next) {
       nit = item_of<RING>(a, tabs, nxt, gy);
-      item_ops<D, G, XP, RING>(a, nit, lane, w, nop);
+      item_ops<D, G, XP, XI, RING>(a, nit, lane, w, nop);
     }
     if constexpr (FUSE) {
       if (pend_b >= 0) count_pending();
@@ -1340,7 +1633,8 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     // (exact-split path: every wave is past the barrier above, so no tile reads the
     // query operands any more; the loop-top barrier publishes the new ones)
     if constexpr (XP) {
-      if constexpr (G == 4) xqueries4(nop.q, a.qscale, lane, w, x_q);
+      if constexpr (XI) wq = iqueries(nop.q, a.qscale, lane, w, reinterpret_cast<u32x4*>(x_q));
+      else if constexpr (G == 4) xqueries4(nop.q, a.qscale, lane, w, x_q);
       else xqueries(nop.q, a.qscale, lane, w, x_q);
     }
     it = nit;
@@ -1503,9 +1797,9 @@ hipError_t decode_launch_split_x(const DecodeArgs& a, hipStream_t s) {
 
 template <int KVT, int D, int G>
 hipError_t decode_launch_split(const DecodeArgs& a, hipStream_t s) {
-  // the exact bf16-split tiles serve fp8 pools at D = 128, G = 8, and bf16 pools at
-  // D = 128, G = 4, with pages of >= 16 (a 16-key half never straddles a page)
-  if constexpr ((kv_fp8(KVT) && D == 128 && G == 8) || (KVT == KV_BF16 && D == 128 && G == 4)) {
+  // the exact-split tiles serve fp8 pools at D = 128, G = 8, and bf16 and int8 pools at
+  // D = 128, G = 4, with pages of >= 16 (a 16-key group never straddles a page)
+  if constexpr ((kv_fp8(KVT) && D == 128 && G == 8) || ((KVT == KV_BF16 || KVT == KV_INT8) && D == 128 && G == 4)) {
     if (a.pool.page_size >= 16) return decode_launch_split_x<KVT, D, G, true>(a, s);
   }
   return decode_launch_split_x<KVT, D, G, false>(a, s);
@@ -1531,11 +1825,11 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Keys per split (measured on the c2, c2r and c5 layers): 4,096 for fp8 pools, 1,024
-// for bf16 pools on the G = 4 exact-split tile, 512 for the register tiles; a split's
-// table entries sit one per lane, so it spans at most 64 pages.
+// Keys per split (measured on the c2, c2r, c2i and c5 layers): 4,096 for fp8 pools,
+// 1,024 for bf16 and int8 pools on the G = 4 exact-split tiles, 512 for the register
+// tiles; a split's table entries sit one per lane, so it spans at most 64 pages.
 int decode_split_keys(int kv_dtype, int group, int head_dim, int page_size) {
-  const bool x4 = kv_dtype == KV_BF16 && group == 4 && head_dim == 128 && page_size >= 16;
+  const bool x4 = (kv_dtype == KV_BF16 || kv_dtype == KV_INT8) && group == 4 && head_dim == 128 && page_size >= 16;
   const int want = kv_fp8(kv_dtype) ? 4096 : (x4 ? 1024 : 512);
   return want < 64 * page_size ? want : 64 * page_size;
 }

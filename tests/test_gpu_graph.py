@@ -3,8 +3,9 @@
 The step (KV_CACHE_WRITE of the new rows, then the decode call) is captured once and
 replayed several times, with eager calls and synchronisations between the replays;
 after every replay the output and the whole pool equal the eager step's bit for bit.
-Both decode kernels are covered (the register tile and the exact-split tiles at G = 4
-and G = 8), which between them make every kind of launch a decode call makes.
+Both decode kernels are covered (the register tile and the exact-split tiles: bf16 and
+int8 at G = 4, fp8 at G = 8), which between them make every kind of launch a decode
+call makes.
 """
 import pytest
 
@@ -18,7 +19,8 @@ CASES = [
     ("g4_bf16_exact_split", [1, 513, 3000, 40], 8, 2, 128, 16, "bf16"),
     ("g8_fp8_exact_split", [4097, 900, 70], 16, 2, 128, 64, "fp8"),
     ("g2_bf16_register_tile", [300, 1500, 17], 4, 2, 128, 16, "bf16"),
-    ("g4_int8_register_tile_merge_kernel", [2000, 33], 8, 2, 128, 16, "int8"),
+    ("g8_int8_register_tile_merge_kernel", [2000, 33], 16, 2, 128, 16, "int8"),
+    ("g4_int8_integer_tile", [2000, 33, 1100], 8, 2, 128, 16, "int8"),
 ]
 
 

@@ -177,6 +177,13 @@ DECODE_CASES = [
     ("g8_fp8_64_groups", [5000, 0, 9000], 512, 64, 128, 64, "fp8", 0),
     # and with 65: a merge kernel follows the split kernel
     ("g8_fp8_65_groups", [0, 4500, 9000, 1], 520, 65, 128, 64, "fp8", 0),
+    # the int8 integer-MFMA tile (G = 4, D = 128, pages >= 16): 64-key tiles, 1,024-key
+    # splits merged in place
+    ("g4_int8_split_edges", [63, 64, 65, 1023, 1024, 1025, 2047, 2049, 4100], 8, 2, 128, 16, "int8", 0),
+    ("g4_int8_window_page32", [3000, 700, 64, 1, 1100], 8, 2, 128, 32, "int8", 1000),
+    ("g4_int8_page64_many_splits", [9000, 0, 5, 2000], 8, 2, 128, 64, "int8", 0),
+    ("g4_int8_16_kv_heads", [1500, 257, 33, 4000, 0, 999], 64, 16, 128, 16, "int8", 0),
+    ("g4_int8_page8_register_tile", [9, 700, 70], 8, 2, 128, 8, "int8", 0),
 ]
 
 
