@@ -69,8 +69,10 @@ template <int KVT, int D, int G> struct DecodePrefetch {
                              : (kv_fp8(KVT) && D == 128 && G == 8) ? 1 : (D == 64 ? 1 : 0);
 };
 
+// tab: the split's table entry first_block + lane; tab2 (int8 tile, whose splits span
+// up to 128 pages): entry first_block + 64 + lane
 struct Split {
-  int kvh, lo, hi, k_end, first_block, tab, lane;
+  int kvh, lo, hi, k_end, first_block, tab, tab2, lane;
 };
 
 // K chunks of this lane's key (kg*4 + j of the tile) and, for fp8, the K/V scales of
@@ -736,13 +738,22 @@ struct IBuf {
   v4f ks, vs;     // scales of keys 16t + 4g .. +3
 };
 
-// (xhalf of quarter qr: the 16-key group from k0 + 16 qr, clamped into [lo, hi])
+// the 16-key group of quarter qr (from k0 + 16 qr, clamped into [lo, hi]), whose block
+// is entry 0 .. 127 of the split
+__device__ __forceinline__ XHalf xquarter(const DecodeArgs& a, const Split& sp, int k0, int qr) {
+  XHalf r;
+  r.hk0 = clampi(k0 + 16 * qr, sp.lo & ~15, sp.hi & ~15);
+  const int local = clampi((r.hk0 >> a.pool.page_shift) - sp.first_block, 0, 127);
+  const int page = local < 64 ? page_uniform(sp.tab, local) : page_uniform(sp.tab2, local - 64);
+  r.ph = (int64_t)page * a.pool.num_kv_heads + sp.kvh;
+  return r;
+}
 __device__ __forceinline__ void iload_k(IBuf& t, const DecodeArgs& a, const Split& sp, int k0) {
   constexpr int NC = 128 / 16;
   const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
 #pragma unroll
   for (int qr = 0; qr < 4; ++qr) {
-    const XHalf x = xhalf(a, sp, k0, qr);
+    const XHalf x = xquarter(a, sp, k0, qr);
     const uint4* kb = reinterpret_cast<const uint4*>(a.pool.k) + x.ph * NC * S + (x.hk0 & (S - 1)) + (g * S + c);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -754,7 +765,7 @@ __device__ __forceinline__ void iload_v(IBuf& t, const DecodeArgs& a, const Spli
   const int S = a.pool.page_size, c = sp.lane & 15, g = sp.lane >> 4;
 #pragma unroll
   for (int qr = 0; qr < 4; ++qr) {
-    const XHalf x = xhalf(a, sp, k0, qr);
+    const XHalf x = xquarter(a, sp, k0, qr);
     const unsigned char* vb = reinterpret_cast<const unsigned char*>(a.pool.v) + (x.ph * S + (x.hk0 & (S - 1))) * D +
                               (4 * g * D + 8 * c);
 #pragma unroll
@@ -764,7 +775,9 @@ __device__ __forceinline__ void iload_v(IBuf& t, const DecodeArgs& a, const Spli
 __device__ __forceinline__ void iload_scales(IBuf& t, const DecodeArgs& a, const Split& sp, int k0, bool kside) {
   const int S = a.pool.page_size, sh = a.pool.page_shift, c = sp.lane & 15, g = sp.lane >> 4;
   const int g0 = clampi(k0 + 16 * (c >> 2) + 4 * g, sp.lo & ~3, sp.hi & ~3);
-  const int page = page_of_lane(sp.tab, clampi((g0 >> sh) - sp.first_block, 0, 63));
+  const int local = clampi((g0 >> sh) - sp.first_block, 0, 127);
+  const int p1 = page_of_lane(sp.tab, local & 63), p2 = page_of_lane(sp.tab2, local & 63);
+  const int page = local < 64 ? p1 : p2;
   const int64_t si = ((int64_t)page * a.pool.num_kv_heads + sp.kvh) * S + (g0 & (S - 1));
   if (kside) t.ks = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.k_scale + si));
   else t.vs = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.pool.v_scale + si));
@@ -1080,7 +1093,7 @@ __device__ __forceinline__ Item item_of_lds(const DecodeArgs& a, const ItemTable
 // loads issued for the next item are not waited on before then.
 template <int NQR>
 struct ItemOps {
-  int tab;
+  int tab, tab2;  // (tab2: int8 tile only)
   float q[NQR];
 };
 
@@ -1108,6 +1121,10 @@ __device__ __forceinline__ void item_ops(const DecodeArgs& a, const Item& it, in
   const int first_block = (it.split * a.split_keys) >> a.pool.page_shift;
   const int entry = RING ? (first_block + lane) % a.ring : min(first_block + lane, a.max_blocks - 1);
   op.tab = a.block_tables[(int64_t)it.b * a.max_blocks + entry];
+  if constexpr (XI) {
+    const int e2 = RING ? (first_block + 64 + lane) % a.ring : min(first_block + 64 + lane, a.max_blocks - 1);
+    op.tab2 = a.block_tables[(int64_t)it.b * a.max_blocks + e2];
+  }
   if constexpr (XI) {
     // lane (c, g): head c % 4 of the group, d = 16g .. 16g + 15 and 64 + 16g .. + 15
     const int c = lane & 15, g = lane >> 4;
@@ -1419,6 +1436,7 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
     sp.kvh = kvh; sp.lo = ss.lo; sp.hi = ss.hi; sp.k_end = k_end; sp.lane = lane;
     sp.first_block = (it.split * a.split_keys) >> a.pool.page_shift;
     sp.tab = clampi(op.tab, 0, a.pool.num_pages - 1);
+    sp.tab2 = XI ? clampi(op.tab2, 0, a.pool.num_pages - 1) : 0;
 
     float m = -INFINITY, l = 0.0f;
     int k0 = k_begin + w * TKW;
@@ -1826,12 +1844,16 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 // Keys per split (measured on the c2, c2r, c2i and c5 layers): 4,096 for fp8 pools,
-// 1,024 for bf16 and int8 pools on the G = 4 exact-split tiles, 512 for the register
-// tiles; a split's table entries sit one per lane, so it spans at most 64 pages.
+// 1,024 for bf16 pools on the G = 4 exact-split tile, 2,048 for int8 pools on the
+// int8 tile (as many bytes per item as the bf16 tile's), 512 for the register tiles.
+// A split's table entries sit one per lane, so it spans at most 64 pages (128 on the
+// int8 tile, two per lane).
 int decode_split_keys(int kv_dtype, int group, int head_dim, int page_size) {
   const bool x4 = (kv_dtype == KV_BF16 || kv_dtype == KV_INT8) && group == 4 && head_dim == 128 && page_size >= 16;
-  const int want = kv_fp8(kv_dtype) ? 4096 : (x4 ? 1024 : 512);
-  return want < 64 * page_size ? want : 64 * page_size;
+  const bool xi = x4 && kv_dtype == KV_INT8;
+  const int want = kv_fp8(kv_dtype) ? 4096 : (xi ? 2048 : (x4 ? 1024 : 512));
+  const int most = (xi ? 128 : 64) * page_size;
+  return want < most ? want : most;
 }
 
 // Batches larger than DECODE_BATCH_CHUNK run as consecutive launches over slices of
