@@ -734,7 +734,7 @@ __device__ __forceinline__ void xqueries4(const float (&qraw)[8], float qscale, 
 // are read from a key inside, so that they are finite.
 struct IBuf {
   u32x4 k[4][2];  // [quarter][step]: key 16 * quarter + c, chunk 4 * step + g
-  u32x2 v[4][4];  // [quarter][r]: key 16 * quarter + 4g + r at d 8c .. 8c + 7
+  uint32_t v[4][4][2];  // [quarter][r]: key 16 * quarter + 4g + r at d 8c .. 8c + 7
   v4f ks, vs;     // scales of keys 16t + 4g .. +3
 };
 
@@ -769,7 +769,11 @@ __device__ __forceinline__ void iload_v(IBuf& t, const DecodeArgs& a, const Spli
     const unsigned char* vb = reinterpret_cast<const unsigned char*>(a.pool.v) + (x.ph * S + (x.hk0 & (S - 1))) * D +
                               (4 * g * D + 8 * c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) t.v[qr][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + r * D));
+    for (int r = 0; r < 4; ++r) {
+      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + r * D));
+      t.v[qr][r][0] = w[0];
+      t.v[qr][r][1] = w[1];
+    }
   }
 }
 __device__ __forceinline__ void iload_scales(IBuf& t, const DecodeArgs& a, const Split& sp, int k0, bool kside) {
@@ -834,19 +838,31 @@ __device__ __forceinline__ float iqueries(const float (&qraw)[32], float qscale,
   return __builtin_ldexpf(1.0f, e - 6 - 7 * t);
 }
 
-// One 64-key tile on the operands in t (each part reloaded with the next tile's once
-// used); qs: the item's Q limb operands in LDS ([d step][lane]); wq: this lane's score
-// weight; o: [d tile].  Lazy running max as in xtile.  l is this lane's part: the item's
-// sum runs over the head's 16 lanes.
-template <typename Hook = NoHook>
+// One 64-key tile on the operands in t; MORE: each part of t is reloaded with the next
+// tile's (from k_next) once used (a compile-time choice: loads under a run-time
+// condition made the compiler copy the loaded registers at the loop's end, which waits
+// for every load in flight).  qs: the item's Q limb operands in LDS ([d step][lane]);
+// wq: this lane's score weight; o: [d tile].  Lazy running max as in xtile.  l is this
+// lane's part: the item's sum runs over the head's 16 lanes.
+template <bool MORE, typename Hook = NoHook>
 __device__ __forceinline__ void itile(const DecodeArgs& a, const Split& sp, IBuf& t, int k0, int k_next,
                                       const u32x4* qs, float wq, v4f (&o)[8], float& m, float& l,
                                       Hook hook = Hook()) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const int c = sp.lane & 15, g = sp.lane >> 4, term = c >> 2;
   const bool b0 = term & 1, b1 = term & 2;
-  const bool more = k_next <= sp.k_end;
+  constexpr bool more = MORE;
   hook();  // (as in xtile4)
+  // ---- V of this tile into B operand order (byte n of each key's 8 for d tile n =
+  // 4hw + i), so the next tile's V loads can go out now
+  uint32_t vt[2][4][4];  // [hw][quarter][i]
+#pragma unroll
+  for (int hw = 0; hw < 2; ++hw)
+#pragma unroll
+    for (int qr = 0; qr < 4; ++qr)
+      transpose4x4(t.v[qr][0][hw], t.v[qr][1][hw], t.v[qr][2][hw], t.v[qr][3][hw], vt[hw][qr]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (more) iload_v(t, a, sp, k_next);
   // ---- scores: limb sums of keys 16qr + 4g + r, weighted
   const i32x4 q0 = __builtin_bit_cast(i32x4, qs[sp.lane]), q1 = __builtin_bit_cast(i32x4, qs[64 + sp.lane]);
   float sw[4][4];
@@ -943,14 +959,7 @@ __device__ __forceinline__ void itile(const DecodeArgs& a, const Split& sp, IBuf
   float wv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) wv[r] = __builtin_ldexpf(1.0f, __builtin_amdgcn_readlane(E, r) - 6 - 7 * g);
-  // ---- values: B operand of d tile n = 4hw + i: byte n of each key's 8
-  uint32_t vt[2][4][4];  // [hw][quarter][i]
-#pragma unroll
-  for (int hw = 0; hw < 2; ++hw)
-#pragma unroll
-    for (int qr = 0; qr < 4; ++qr)
-      transpose4x4(t.v[qr][0][hw], t.v[qr][1][hw], t.v[qr][2][hw], t.v[qr][3][hw], vt[hw][qr]);
-  if (more) iload_v(t, a, sp, k_next);
+  // ---- values
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int hw = n >> 2, i = n & 3;
@@ -1450,16 +1459,17 @@ __global__ __launch_bounds__(64 * DecodeWaves<XP>::value, (DecodeOcc<KVT, XP>::v
       if constexpr (XI) {
         const u32x4* qi = reinterpret_cast<const u32x4*>(x_q);
         IBuf ib;
+        k0 = uni(k0);  // (wave-uniform: the page lookups stay scalar)
         if (k0 <= k_end) {
           iload_k(ib, a, sp, k0);
           iload_scales(ib, a, sp, k0, true);
           iload_scales(ib, a, sp, k0, false);
           iload_v(ib, a, sp, k0);
           while (k0 + STEP <= k_end) {
-            itile(a, sp, ib, k0, k0 + STEP, qi, wq, ox, m, l);
+            itile<true>(a, sp, ib, k0, k0 + STEP, qi, wq, ox, m, l);
             k0 += STEP;
           }
-          itile(a, sp, ib, k0, k0 + STEP, qi, wq, ox, m, l, claim);
+          itile<false>(a, sp, ib, k0, k0 + STEP, qi, wq, ox, m, l, claim);
         } else {
           claim();
         }
