@@ -695,36 +695,45 @@ def clock_summary(d: str, kernels: str, command: str):
 def stats_summary(d: str, configs: str, warmup: str, steps: str, command: str):
     """Per-kernel durations from rocprofv3 --kernel-trace of one bench run, per workload.
 
-    The run executes the workloads in the order given; each makes `warmup` attention
-    calls, then `steps` back-to-back calls (the contract loop), then `steps` calls each
-    after a cache-evicting read (the calls the roofline is taken from).  Dispatches of
-    the attention kernels are assigned to the workloads and phases in that order.  The
-    history-write dispatches (write_kernel) of a decode workload's flushed write timing
-    are listed per workload as well."""
+    The run executes the workloads in the order given.  A prefill or GDN workload makes
+    `warmup` attention calls, then `steps` back-to-back calls (the contract loop), then
+    `steps` calls each after a cache-evicting read (the calls the roofline is taken
+    from).  A decode workload makes `warmup` eager steps and `steps` timed eager steps,
+    one eager step and one replay to check the captured graph, `warmup` replays, the
+    `steps` replayed steps of the contract loop, then the `steps` flushed calls.
+    Dispatches of the attention kernels are assigned to the workloads and phases in that
+    order; the contract loop is listed as back to back."""
     import csv
+    from paged_kv_attention_cache_amd import workloads as W
     rows = sorted(csv.DictReader(open(_find_csv(d, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"]))
     w, k = int(warmup), int(steps)
-    n = w + 2 * k
     att = [r for r in rows if any(x in r["Kernel_Name"] for x in ATTN_KERNELS)]
     mains = [i for i, r in enumerate(att) if any(x in r["Kernel_Name"] for x in
                                                  ("decode_split_kernel", "prefill_kernel", "gdn_decode_kernel"))]
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
     print(f"command: {command}\n")
-    print(f"Durations from the kernel trace, grouped by workload.  Per workload: {w} warm-up calls, {k} "
-          f"back-to-back calls, then {k} calls each after a 512 MiB cache-evicting read (the roofline's calls).\n")
+    print(f"Durations from the kernel trace, grouped by workload.  Per workload: {w} warm-up calls, the "
+          f"{k} back-to-back calls of the contract loop (for decode, {k} replays of the captured step, after "
+          f"{w} eager and {k} timed eager steps, a check and {w} warm-up replays), then {k} calls each after a "
+          f"512 MiB cache-evicting read (the roofline's calls).\n")
     print("| workload | kernel | flushed calls: average us | median us | min us | back-to-back average us |")
     print("|---|---|---|---|---|---|")
     lists = []
-    for ci, cfg in enumerate(configs.split(",")):
-        blk = mains[ci * n:(ci + 1) * n]
+    pos = 0
+    for cfg in configs.split(","):
+        decode = getattr(W.make(cfg), "kind", "gdn") == "decode"
+        n = 2 * w + 3 * k + 2 if decode else w + 2 * k
+        blk = mains[pos:pos + n]
         if len(blk) < n:
             break
-        hi = mains[(ci + 1) * n] if (ci + 1) * n < len(mains) else len(att)
-        phase_start = [blk[0], blk[w], blk[w + k], hi]
+        hi = mains[pos + n] if pos + n < len(mains) else len(att)
+        b0 = 2 * w + k + 2 if decode else w  # first back-to-back call of the contract loop
+        phase_start = [blk[b0], blk[b0 + k], hi]
+        pos += n
         per = {}
-        for ph in (1, 2):
+        for ph in (0, 1):
             for r in att[phase_start[ph]:phase_start[ph + 1]]:
-                per.setdefault(_short_name(r["Kernel_Name"]), ([], []))[ph - 1].append(dur(r))
+                per.setdefault(_short_name(r["Kernel_Name"]), ([], []))[ph].append(dur(r))
         tot_f = tot_b = 0.0
         for name, (b2b, fl) in per.items():
             tot_f += float(np.mean(fl))
