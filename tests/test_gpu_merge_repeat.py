@@ -1,11 +1,11 @@
 """The in-place merge of decode splits, repeated.
 
-On the exact-split decode kernels (bf16 at G = 4, fp8 at G = 8) the workgroup that
-stores a (sequence, head group)'s last split merges all of its splits, reading the
-other workgroups' partial states after an arrival counter says they are all stored.
-Its correctness rests on ordering (coherent stores, a wait for their completion
-before the count, loads issued only after the count has returned), so a rare
-ordering failure would show as a call whose output differs from the others.  Each
+On the exact-split decode kernels (bf16 and int8 at G = 4, fp8 at G = 8) the
+workgroup that stores a (sequence, head group)'s last split merges all of its splits,
+reading the other workgroups' partial states after an arrival counter says they are
+all stored.  Its correctness rests on ordering (coherent stores, a wait for their
+completion before the count, loads issued only after the count has returned), so a
+rare ordering failure would show as a call whose output differs from the others.  Each
 workload below is decoded 200 times back to back on one workspace, and every output
 must equal the first one bit for bit (the first one is checked against the oracle
 elsewhere); the loop stops at the first mismatch.
@@ -37,7 +37,7 @@ def _repeat(torch, st):
     return first
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c5"])
+@pytest.mark.parametrize("cfg", ["c2", "c5", "c2i"])
 def test_in_place_merge_gives_the_same_bits_on_every_call(torch_cuda, cfg):
     torch = torch_cuda
     wl = W.make(cfg)
