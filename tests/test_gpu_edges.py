@@ -184,7 +184,8 @@ def test_windowed_prefill_and_decode_ignore_unwritten_nan_rows(torch_cuda, kv_dt
     assert np.all(np.isfinite(got)), "prefill read an unwritten row into its sums"
     assert row_rel_err(got, oracle.prefill(op, q, wl.block_tables, pos, win, wl.scale)) <= TOL[kv_dtype]
     # decode of the last position, on a pool written only inside its own window (fp8 at
-    # G = 8 takes the exact-split kernel, the others the register-tile kernel)
+    # G = 8 and bf16 and int8 at G = 4 take the exact-split tiles, the others the
+    # register tile)
     L = np.array([start + chunk], np.int32)
     gp, op = _pools_written_from(tl, torch, wl, int(L[0]) - win)
     qd = np.ascontiguousarray(q[:, -1])
