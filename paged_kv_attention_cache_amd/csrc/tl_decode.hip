@@ -730,8 +730,10 @@ __device__ __forceinline__ void xqueries4(const float (&qraw)[8], float qscale, 
 // its A operand as loaded.  V rows are loaded 8 bytes (d 8c .. 8c + 7) per key; the B
 // operand of d tile n takes byte n of each of the lane's 16 keys, a 4 x 4 byte transpose
 // per quarter and half row.  Codes of keys outside [lo, hi] are read from the same
-// page (an int8 code is never NaN) and multiplied by zero limbs or masked; their scales
-// are read from a key inside, so that they are finite.
+// page (an int8 code is never NaN) and meet zero limbs or a masked score.  Scales are
+// read in 4-key groups clamped into [lo, hi] rounded out to 4; a group's keys outside
+// [lo, hi] may hold scales never written, so a masked key's K scale never reaches a
+// used score and its probability stays exactly 0, not 0 times its V scale.
 struct IBuf {
   u32x4 k[4][2];  // [quarter][step]: key 16 * quarter + c, chunk 4 * step + g
   uint32_t v[4][4][2];  // [quarter][r]: key 16 * quarter + 4g + r at d 8c .. 8c + 7
@@ -911,7 +913,7 @@ __device__ __forceinline__ void itile(const DecodeArgs& a, const Split& sp, IBuf
   for (int r = 0; r < 4; ++r) {
     const float p = fast_exp2(s4[r] - m_use);
     psum += p;
-    pv[r] = p * t.vs[r];
+    pv[r] = p > 0.0f ? p * t.vs[r] : 0.0f;
     pmax = fmaxf(pmax, pv[r]);
   }
   l = l * alpha + psum;
